@@ -1,0 +1,17 @@
+"""NVFP4 routed-MoE FFN layer for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``libmoe_nvfp4.so`` (C ABI in
+``include/moe_nvfp4.h``); ``ops`` is its thin Python binding.
+"""
+from .ops import (  # noqa: F401
+    MOE_ACT_BF16,
+    MOE_ACT_FP8_ROW,
+    NVFP4Weights,
+    moe_combine,
+    moe_expert_ffn,
+    moe_init,
+    moe_layer,
+    moe_permute,
+    moe_route_topk,
+    workspace_bytes,
+)

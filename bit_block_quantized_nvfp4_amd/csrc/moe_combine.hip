@@ -1,0 +1,61 @@
+// Combine (A10): out[t] = bf16( sum_k w[t][k] * y[slot_pos[t*K+k]] + y[slot_pos[T*K+t]] ),
+// fp32 accumulation in slot order then the shared expert, one rounding at the
+// end.  The order is fixed per element and independent of how the grid is cut
+// (the same-order rule for per-slot expert outputs of the issue "EXL3
+// Qwen3.8-Flash-Next on CUDA sm_120 ...", expert-parallel TP=2).
+// Each thread owns 8 consecutive columns of one token (16-byte loads/stores).
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
+                                                 const float* __restrict__ w,
+                                                 const int32_t* __restrict__ slot_pos, int T,
+                                                 int K, int H, int has_shared,
+                                                 uint16_t* __restrict__ out) {
+  const int cpr = H / 8;  // 8-column chunks per row
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long)T * cpr) return;
+  const int t = (int)(gid / cpr), c = (int)(gid % cpr);
+  const int TK = T * K;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int p = slot_pos[(size_t)t * K + k];
+    if (p < 0 || p >= TK) continue;
+    const float wt = w[(size_t)t * K + k];
+    const u32x4 v = *(const u32x4*)(y + (size_t)p * H + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = fmaf(wt, bf16_bits_to_f32(v[j] & 0xFFFFu), acc[2 * j]);
+      acc[2 * j + 1] = fmaf(wt, bf16_bits_to_f32(v[j] >> 16), acc[2 * j + 1]);
+    }
+  }
+  const int ps = has_shared ? slot_pos[(size_t)TK + t] : -1;
+  if (ps >= 0 && ps < TK + T) {
+    const u32x4 v = *(const u32x4*)(y + (size_t)ps * H + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += bf16_bits_to_f32(v[j] & 0xFFFFu);
+      acc[2 * j + 1] += bf16_bits_to_f32(v[j] >> 16);
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+  *(u32x4*)(out + (size_t)t * H + 8 * c) = o;
+}
+
+void register_combine_kernels(std::vector<const void*>& k) { k.push_back((const void*)&k_combine); }
+
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos, int T,
+                          int K, int H, int has_shared, uint16_t* out, hipStream_t s) {
+  const long n = (long)T * (H / 8);
+  MOE_LAUNCH("combine", s, k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, w,
+             slot_pos, T, K, H, has_shared, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

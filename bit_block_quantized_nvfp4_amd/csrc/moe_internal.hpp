@@ -1,0 +1,55 @@
+// Host-side declarations shared by the library's translation units: kernel
+// launchers (one per kernel family), the kernel registry used by moe_init(),
+// and the launch bracket used for per-kernel timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/moe_nvfp4.h"
+
+namespace moe {
+
+// Per-kernel timing (see moe_timing_* in the public header). timing_begin
+// returns a record slot (or -1 when timing is off) that timing_end closes.
+int timing_begin(const char* name, hipStream_t s);
+void timing_end(int slot, hipStream_t s);
+
+#define MOE_LAUNCH(name, stream, ...)                 \
+  do {                                                \
+    int moe_slot_ = ::moe::timing_begin(name, stream); \
+    hipLaunchKernelGGL(__VA_ARGS__);                  \
+    ::moe::timing_end(moe_slot_, stream);             \
+  } while (0)
+
+// Kernel registries: every translation unit lists its __global__ functions so
+// that moe_init() can resolve each of them once.
+void register_route_kernels(std::vector<const void*>& k);
+void register_permute_kernels(std::vector<const void*>& k);
+void register_combine_kernels(std::vector<const void*>& k);
+void register_ffn_kernels(std::vector<const void*>& k);
+
+// Launchers. Arguments are validated by the C entry points before these run.
+hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                             hipStream_t s);
+
+size_t permute_workspace_bytes(int T, int E, int K);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_shared,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                          int32_t* slot_pos, void* ws, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos, int T,
+                          int K, int H, int has_shared, uint16_t* out, hipStream_t s);
+
+size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode);
+hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                             const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
+                             uint16_t* y_slots, void* ws, hipStream_t s);
+
+// Decode/prefill switch of moe_expert_ffn: T <= kDecodeMaxT uses the GEMV path.
+constexpr int kDecodeMaxT = 8;
+
+}  // namespace moe

@@ -1,0 +1,229 @@
+// Expert permutation (A2): counts, offsets, sorted_slot, slot_pos.
+//
+// The position of routed slot s in expert group e is
+//   offsets[e] + #{ s' < s : ids[s'] == e },
+// i.e. a stable counting sort.  The rank inside a chunk of 256 slots is taken
+// from per-wave 64-bit masks in LDS: lane l of wave w sets bit l of
+// mask[w][e]; the slot's rank among same-expert slots of the chunk is the
+// popcount of the masks of the lower waves plus the popcount of its own wave's
+// mask below bit l.  Atomics only ever OR bits or add integer counts, so no
+// result depends on timing.
+//
+// Two paths:
+//  * T*K <= kSmallSlots: one workgroup does count, scan and scatter (decode);
+//  * otherwise three kernels over tiles of kTileSlots slots: per-tile
+//    histograms, a per-expert scan over tiles, and the scatter (every scatter
+//    block re-derives the expert offsets from the per-expert totals).
+#include "moe_device.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+
+constexpr int kBlock = 256;           // 4 waves
+constexpr int kChunk = 256;           // slots ranked at once
+constexpr int kTileSlots = 4 * kChunk;
+constexpr int kSmallSlots = 2048;
+constexpr int kMaxE = 1024;
+
+// Exclusive scan, in place, of a[0..n) held in LDS, by a 256-thread block.
+// Returns the total.  Must be called by every thread of the block.
+__device__ int block_exclusive_scan(int* a, int n, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + kBlock - 1) / kBlock;
+  const int lo = min(tid * per, n), hi = min(lo + per, n);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += a[i];
+  const int incl = wave_incl_scan(local, lane);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kBlock / 64; ++i) {
+    before += (i < wv) ? wsum[i] : 0;
+    total += wsum[i];
+  }
+  int run = before + incl - local;
+  for (int i = lo; i < hi; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Ranks one chunk of up to 256 slots starting at c0 and scatters them.
+// run[e] holds the next free position of group e and is advanced here.
+__device__ void scatter_chunk(const int32_t* __restrict__ ids, int TK, int E, int c0,
+                              unsigned long long (*masks)[kMaxE], int* run,
+                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int s = c0 + tid;
+  const bool in = s < TK;
+  const int e = in ? ids[s] : -1;
+  const bool ok = in && e >= 0 && e < E;
+  const unsigned long long bit = 1ull << lane;
+  if (ok) atomicOr(&masks[wv][e], bit);
+  __syncthreads();
+  int pos = -1;
+  bool last = false;
+  int tot = 0;
+  if (ok) {
+    int before = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kBlock / 64; ++w2) {
+      const int c = __popcll(masks[w2][e]);
+      before += (w2 < wv) ? c : 0;
+      tot += c;
+    }
+    const int r = before + __popcll(masks[wv][e] & (bit - 1));
+    pos = run[e] + r;
+    last = (r == tot - 1);
+    sorted_slot[pos] = s;
+  }
+  if (in) slot_pos[s] = pos;
+  __syncthreads();
+  if (ok) {
+    masks[wv][e] = 0ull;
+    if (last) run[e] += tot;
+  }
+  __syncthreads();
+}
+
+// The shared group: slot T*K + t sits at position off_shared + t, both ways.
+__device__ void write_shared_group(int T, int TK, int off_shared, int32_t* __restrict__ sorted_slot,
+                                   int32_t* __restrict__ slot_pos, int first, int stride) {
+  for (int t = first; t < T; t += stride) {
+    sorted_slot[off_shared + t] = TK + t;
+    slot_pos[TK + t] = off_shared + t;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_permute_small(
+    const int32_t* __restrict__ ids, int T, int E, int K, int has_shared,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  __shared__ unsigned long long masks[kBlock / 64][kMaxE];
+  __shared__ int run[kMaxE + 2];
+  __shared__ int wsum[kBlock / 64];
+  const int tid = threadIdx.x;
+  const int TK = T * K, G = E + has_shared;
+  for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
+  for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : 0;
+  __syncthreads();
+  for (int s = tid; s < TK; s += kBlock) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&run[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < G; e += kBlock) counts[e] = run[e];
+  const int total = block_exclusive_scan(run, G, wsum);
+  for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
+  if (tid == 0) offsets[G] = total;
+  const int off_shared = has_shared ? run[E] : 0;  // scatter_chunk only moves run[e < E]
+  for (int c0 = 0; c0 < TK; c0 += kChunk) scatter_chunk(ids, TK, E, c0, masks, run, sorted_slot, slot_pos);
+  if (has_shared) write_shared_group(T, TK, off_shared, sorted_slot, slot_pos, tid, kBlock);
+}
+
+// Tile histograms, written expert-major: cnt[e * ntiles + tile].
+__global__ __launch_bounds__(kBlock) void k_permute_count(const int32_t* __restrict__ ids, int TK,
+                                                         int E, int ntiles,
+                                                         int32_t* __restrict__ cnt) {
+  __shared__ int hist[kMaxE];
+  const int tid = threadIdx.x, tile = blockIdx.x;
+  for (int e = tid; e < E; e += kBlock) hist[e] = 0;
+  __syncthreads();
+  const int s0 = tile * kTileSlots, s1 = min(s0 + kTileSlots, TK);
+  for (int s = s0 + tid; s < s1; s += kBlock) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlock) cnt[(size_t)e * ntiles + tile] = hist[e];
+}
+
+// Per expert: exclusive scan over tiles (in place) and the expert total.
+__global__ __launch_bounds__(kBlock) void k_permute_scan_tiles(int32_t* __restrict__ cnt,
+                                                              int ntiles,
+                                                              int32_t* __restrict__ tot) {
+  __shared__ int buf[kBlock];
+  __shared__ int wsum[kBlock / 64];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  int32_t* row = cnt + (size_t)e * ntiles;
+  int carry = 0;
+  for (int b0 = 0; b0 < ntiles; b0 += kBlock) {
+    const int i = b0 + tid;
+    buf[tid] = (i < ntiles) ? row[i] : 0;
+    __syncthreads();
+    const int sum = block_exclusive_scan(buf, kBlock, wsum);
+    if (i < ntiles) row[i] = carry + buf[tid];
+    carry += sum;
+    __syncthreads();
+  }
+  if (tid == 0) tot[e] = carry;
+}
+
+__global__ __launch_bounds__(kBlock) void k_permute_scatter(
+    const int32_t* __restrict__ ids, int T, int E, int K, int has_shared, int ntiles,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ tot,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+  __shared__ unsigned long long masks[kBlock / 64][kMaxE];
+  __shared__ int run[kMaxE + 2];
+  __shared__ int wsum[kBlock / 64];
+  const int tid = threadIdx.x, tile = blockIdx.x;
+  const int TK = T * K, G = E + has_shared;
+  for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
+  for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : tot[e];
+  __syncthreads();
+  if (tile == 0)
+    for (int e = tid; e < G; e += kBlock) counts[e] = run[e];
+  const int total = block_exclusive_scan(run, G, wsum);
+  if (tile == 0) {
+    for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
+    if (tid == 0) offsets[G] = total;
+  }
+  const int off_shared = has_shared ? run[E] : 0;
+  for (int e = tid; e < E; e += kBlock) run[e] += cnt[(size_t)e * ntiles + tile];
+  __syncthreads();
+  const int s0 = tile * kTileSlots, s1 = min(s0 + kTileSlots, TK);
+  for (int c0 = s0; c0 < s1; c0 += kChunk) scatter_chunk(ids, s1, E, c0, masks, run, sorted_slot, slot_pos);
+  if (has_shared)
+    write_shared_group(T, TK, off_shared, sorted_slot, slot_pos, tile * kBlock + tid, ntiles * kBlock);
+}
+
+void register_permute_kernels(std::vector<const void*>& k) {
+  k.push_back((const void*)&k_permute_small);
+  k.push_back((const void*)&k_permute_count);
+  k.push_back((const void*)&k_permute_scan_tiles);
+  k.push_back((const void*)&k_permute_scatter);
+}
+
+static inline int ntiles_of(int TK) { return (TK + kTileSlots - 1) / kTileSlots; }
+
+size_t permute_workspace_bytes(int T, int E, int K) {
+  const long TK = (long)T * K;
+  if (TK <= kSmallSlots) return 0;
+  return ((size_t)E * ntiles_of((int)TK) + (size_t)E) * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_shared,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                          int32_t* slot_pos, void* ws, hipStream_t s) {
+  const int TK = T * K;
+  if (TK <= kSmallSlots) {
+    MOE_LAUNCH("permute_small", s, k_permute_small, dim3(1), dim3(kBlock), 0, s, ids, T, E, K,
+               has_shared, counts, offsets, sorted_slot, slot_pos);
+    return hipGetLastError();
+  }
+  const int nt = ntiles_of(TK);
+  int32_t* cnt = (int32_t*)ws;
+  int32_t* tot = cnt + (size_t)E * nt;
+  MOE_LAUNCH("permute_count", s, k_permute_count, dim3(nt), dim3(kBlock), 0, s, ids, TK, E, nt, cnt);
+  MOE_LAUNCH("permute_scan_tiles", s, k_permute_scan_tiles, dim3(E), dim3(kBlock), 0, s, cnt, nt, tot);
+  MOE_LAUNCH("permute_scatter", s, k_permute_scatter, dim3(nt), dim3(kBlock), 0, s, ids, T, E, K,
+             has_shared, nt, cnt, tot, counts, offsets, sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,189 @@
+"""Python binding of the C ABI (include/moe_nvfp4.h): argument marshalling only.
+
+Every function takes and returns torch tensors on the current HIP device and
+enqueues the library's kernels on torch's current stream.  Outputs (and, unless
+given, workspaces) are allocated with torch; all arithmetic runs in the HIP
+kernels of libmoe_nvfp4.so.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_PERMUTE, check
+
+__all__ = [
+    "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
+    "moe_combine", "moe_layer", "workspace_bytes", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
+]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, shape=None, name="tensor"):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+@dataclass
+class NVFP4Weights:
+    """A device-resident NVFP4 expert bank in the layout of moe_nvfp4_weights."""
+    gu_codes: torch.Tensor   # uint8 [E', 2I, H/2]
+    gu_scales: torch.Tensor  # uint8 [E', 2I, H/16]
+    dn_codes: torch.Tensor   # uint8 [E', H, I/2]
+    dn_scales: torch.Tensor  # uint8 [E', H, I/16]
+    scale2: torch.Tensor     # float32 [E', 3]
+    E: int
+    H: int
+    I: int
+    has_shared: bool
+
+    @classmethod
+    def from_bank(cls, bank, device="cuda") -> "NVFP4Weights":
+        def up(a):
+            return torch.from_numpy(a).to(device)
+        return cls(up(bank.gu_codes), up(bank.gu_scales), up(bank.dn_codes), up(bank.dn_scales),
+                   up(bank.scale2), bank.E, bank.H, bank.I, bool(bank.has_shared))
+
+    def struct(self) -> _lib.MoeNvfp4Weights:
+        G, H, I = self.E + int(self.has_shared), self.H, self.I
+        _need(self.gu_codes, torch.uint8, (G, 2 * I, H // 2), "gu_codes")
+        _need(self.gu_scales, torch.uint8, (G, 2 * I, H // 16), "gu_scales")
+        _need(self.dn_codes, torch.uint8, (G, H, I // 2), "dn_codes")
+        _need(self.dn_scales, torch.uint8, (G, H, I // 16), "dn_scales")
+        _need(self.scale2, torch.float32, (G, 3), "scale2")
+        return _lib.MoeNvfp4Weights(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
+                                    self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
+                                    self.scale2.data_ptr(), self.E, H, I, int(self.has_shared))
+
+
+def moe_init() -> None:
+    check(_lib.lib().moe_init())
+
+
+def workspace_bytes(op: int, T: int, E: int, K: int, H: int = 0, I: int = 0,
+                    has_shared: bool = False, act_mode: int = MOE_ACT_BF16) -> int:
+    return int(_lib.lib().moe_workspace_bytes(op, T, E, K, H, I, int(has_shared), act_mode))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def moe_route_topk(logits: torch.Tensor, K: int, ids: Optional[torch.Tensor] = None,
+                   w: Optional[torch.Tensor] = None):
+    _need(logits, torch.float32, name="logits")
+    T, E = logits.shape
+    ids = torch.empty((T, K), dtype=torch.int32, device=logits.device) if ids is None else ids
+    w = torch.empty((T, K), dtype=torch.float32, device=logits.device) if w is None else w
+    _need(ids, torch.int32, (T, K), "ids")
+    _need(w, torch.float32, (T, K), "w")
+    check(_lib.lib().moe_route_topk(_ptr(logits), T, E, K, _ptr(ids), _ptr(w), _stream()))
+    return ids, w
+
+
+def moe_permute(ids: torch.Tensor, E: int, has_shared: bool, ws: Optional[torch.Tensor] = None,
+                out=None):
+    _need(ids, torch.int32, name="ids")
+    T, K = ids.shape
+    G = E + int(has_shared)
+    dev = ids.device
+    if out is None:
+        out = (torch.empty(G, dtype=torch.int32, device=dev),
+               torch.empty(G + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * K + (T if has_shared else 0), dtype=torch.int32, device=dev),
+               torch.empty(T * K + (T if has_shared else 0), dtype=torch.int32, device=dev))
+    counts, offsets, sorted_slot, slot_pos = out
+    nb = workspace_bytes(MOE_OP_PERMUTE, T, E, K, 0, 0, has_shared)
+    ws = _workspace(nb, dev, ws)
+    check(_lib.lib().moe_permute(_ptr(ids), T, E, K, int(has_shared), _ptr(counts), _ptr(offsets),
+                                 _ptr(sorted_slot), _ptr(slot_pos), _ptr(ws), nb, _stream()))
+    return counts, offsets, sorted_slot, slot_pos
+
+
+def moe_expert_ffn(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tensor,
+                   sorted_slot: torch.Tensor, act_mode: int = MOE_ACT_BF16,
+                   ws: Optional[torch.Tensor] = None, y_slots: Optional[torch.Tensor] = None,
+                   return_ws: bool = False):
+    _need(x, torch.bfloat16, name="x")
+    T, H = x.shape
+    if H != W.H:
+        raise ValueError("x width does not match the weight bank")
+    S = T * K + (T if W.has_shared else 0)
+    dev = x.device
+    y_slots = torch.empty((S, H), dtype=torch.bfloat16, device=dev) if y_slots is None else y_slots
+    _need(y_slots, torch.bfloat16, (S, H), "y_slots")
+    _need(offsets, torch.int32, (W.E + int(W.has_shared) + 1,), "offsets")
+    _need(sorted_slot, torch.int32, (S,), "sorted_slot")
+    nb = workspace_bytes(MOE_OP_EXPERT_FFN, T, W.E, K, H, W.I, W.has_shared, act_mode)
+    ws = _workspace(nb, dev, ws)
+    st = W.struct()
+    check(_lib.lib().moe_expert_ffn(ctypes.byref(st), _ptr(x), T, K, _ptr(offsets),
+                                    _ptr(sorted_slot), act_mode, _ptr(y_slots), _ptr(ws), nb,
+                                    _stream()))
+    return (y_slots, ws) if return_ws else y_slots
+
+
+def moe_combine(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Tensor, K: int,
+                has_shared: bool, out: Optional[torch.Tensor] = None):
+    _need(y_slots, torch.bfloat16, name="y_slots")
+    _need(w, torch.float32, name="w")
+    T = w.shape[0]
+    H = y_slots.shape[1]
+    _need(slot_pos, torch.int32, (T * K + (T if has_shared else 0),), "slot_pos")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=y_slots.device) if out is None else out
+    _need(out, torch.bfloat16, (T, H), "out")
+    check(_lib.lib().moe_combine(_ptr(y_slots), _ptr(w), _ptr(slot_pos), T, K, H, int(has_shared),
+                                 _ptr(out), _stream()))
+    return out
+
+
+def moe_layer(W: NVFP4Weights, x: torch.Tensor, logits: torch.Tensor, K: int,
+              act_mode: int = MOE_ACT_BF16) -> dict:
+    """One layer call: route -> permute -> expert FFN -> combine, all on the GPU."""
+    ids, w = moe_route_topk(logits, K)
+    counts, offsets, sorted_slot, slot_pos = moe_permute(ids, W.E, W.has_shared)
+    y = moe_expert_ffn(W, x, K, offsets, sorted_slot, act_mode)
+    out = moe_combine(y, w, slot_pos, K, W.has_shared)
+    return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,
+                slot_pos=slot_pos, y_slots=y, out=out)
+
+
+def timing_enable(on: bool = True) -> None:
+    check(_lib.lib().moe_timing_enable(int(on)))
+
+
+def timing_reset() -> None:
+    check(_lib.lib().moe_timing_reset())
+
+
+def timing_read(max_names: int = 32) -> dict:
+    names = (ctypes.c_char_p * max_names)()
+    launches = (ctypes.c_int * max_names)()
+    ms = (ctypes.c_double * max_names)()
+    dropped = ctypes.c_int(0)
+    n = check(_lib.lib().moe_timing_read(names, launches, ms, max_names, ctypes.byref(dropped)))
+    res = {names[i].decode(): (launches[i], ms[i]) for i in range(n)}
+    if dropped.value:
+        res["_dropped"] = (dropped.value, 0.0)
+    return res

@@ -1,0 +1,224 @@
+/*
+ * moe_nvfp4.h -- C ABI of the routed mixture-of-experts FFN layer with NVFP4
+ * weights and bf16 activations, for AMD Instinct MI355X (gfx950).
+ *
+ * One layer call is four entry points, run in this order on one HIP stream:
+ *
+ *   moe_route_topk  -> ids, w          router softmax + top-K per token
+ *   moe_permute     -> counts, offsets, sorted_slot, slot_pos
+ *   moe_expert_ffn  -> y_slots         gate_up GEMM, SiLU*up, down GEMM per
+ *                                      expert group (routed + shared)
+ *   moe_combine     -> out             fixed-order fp32 weighted sum
+ *
+ * Sources.  The operations are the ones listed as the prefill ops of a MoE
+ * layer that can change the logits (router GEMM + top-k, shared expert, routed
+ * experts, combine/unpermute) in the issue "[job] Qwen3.8-Flash-Next:
+ * long-context cold prefill to SGLang parity"; the numerics (NVFP4 dequant as
+ * e2m1 x e4m3 block scale x scale2, f32 accumulation, bf16 SiLU intermediate,
+ * fp32 weighted combine) are the rows of that issue's table attributing the
+ * transposed-MoE perplexity gap.  The tie rule of the router is the one of the
+ * page "handover briefs" (item A1 and the indexer-selection kernel spec).
+ *
+ * Conventions for every entry point:
+ *  - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *    keeps no reference after the call returns.  moe_nvfp4_weights is a host
+ *    struct that holds device pointers.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No entry point synchronises, allocates device memory,
+ *    copies device to host or calls hipMemset, so a whole layer call can be
+ *    captured into a HIP graph.
+ *  - Return value: MOE_OK (0) or a negative status; moe_last_error() then
+ *    holds a message for the calling thread.  Argument errors are detected on
+ *    the host before anything is enqueued.  Faults inside a kernel surface at
+ *    the caller's next synchronisation, as with any HIP kernel.
+ *  - Integer stages are deterministic and bit-exact; floating stages use a
+ *    fixed reduction order (no float atomics), so repeated calls on the same
+ *    inputs give bitwise identical outputs.
+ *
+ * Limits: T >= 1, 1 <= K <= 32, K <= E <= 1024; for the expert FFN H is a
+ * multiple of 256 in [256, 4096] and I a multiple of 128 in [128, 1024]; for
+ * the combine H is a multiple of 8.  The library builds for gfx950
+ * only; moe_init() refuses any other device.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_EINVAL -1         /* null pointer, size out of range, bad combination */
+#define MOE_EUNSUPPORTED -2   /* device is not gfx950, or unknown act_mode/op     */
+#define MOE_EHIP -3           /* a HIP runtime call or kernel launch failed        */
+#define MOE_EWORKSPACE -4     /* workspace smaller than moe_workspace_bytes()      */
+
+/* Activation modes of moe_expert_ffn. */
+#define MOE_ACT_BF16 0        /* gate_up reads the bf16 activations as they are    */
+#define MOE_ACT_FP8_ROW 1     /* gate_up reads per-token-row e4m3 activations      */
+
+/* Operation ids of moe_workspace_bytes. */
+#define MOE_OP_PERMUTE 1
+#define MOE_OP_EXPERT_FFN 2
+
+/*
+ * A bank of NVFP4 experts: E routed experts plus, if has_shared, one shared
+ * expert at index E.  E' = E + has_shared groups, each laid out contiguously
+ * (the resident [N, K/2] layout: one row per output feature, K contiguous):
+ *
+ *   gu_codes  [E'][2I][H/2]  e2m1 codes, two per byte, the low nibble is the
+ *                            even K index; rows 0..I-1 = gate, I..2I-1 = up
+ *   gu_scales [E'][2I][H/16] e4m3 (OCP "fn") scale of each 16 consecutive K
+ *   dn_codes  [E'][H][I/2]
+ *   dn_scales [E'][H][I/16]
+ *   scale2    [E'][3]        fp32 per-tensor scale of gate, up, down
+ *
+ * Dequantised weight: W[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k/16]) * scale2.
+ */
+typedef struct moe_nvfp4_weights {
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint8_t* dn_codes;
+  const uint8_t* dn_scales;
+  const float* scale2;
+  int32_t E;
+  int32_t H;
+  int32_t I;
+  int32_t has_shared;
+} moe_nvfp4_weights;
+
+/*
+ * Check that the current HIP device is gfx950 and that every kernel of the
+ * library is loadable (resolved once here, never per launch).  Returns MOE_OK,
+ * MOE_EUNSUPPORTED (other architecture, the message names it) or MOE_EHIP.
+ * The other entry points call it implicitly on first use per device.
+ */
+int moe_init(void);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Device workspace, in bytes, that `op` needs for these sizes (0 if none).
+ * Returns 0 for invalid sizes; the entry point itself reports the error.
+ */
+size_t moe_workspace_bytes(int op, int T, int E, int K, int H, int I, int has_shared,
+                           int act_mode);
+
+/*
+ * Router top-K: for each token t, rank the E experts by logit (larger first,
+ * equal logits -> lower index first, NaN counts as -inf), put the rank-k
+ * expert in slot k, and weight the K selected experts by the softmax of their
+ * logits: w[t][k] = exp(z_k - z_0) / sum_j exp(z_j - z_0), where a term with
+ * z_k == z_0 is exp(0) = 1 even for infinite logits.  This equals the softmax
+ * over all E experts restricted to the selected K and renormalised.
+ *
+ *   logits [T][E] float32, row-major      (in)
+ *   ids    [T][K] int32                   (out) expert of each slot
+ *   w      [T][K] float32                 (out) routing weight of each slot
+ *
+ * Limits: 1 <= K <= min(E, 32), E <= 1024.  Rows are independent.
+ */
+int moe_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                   void* stream);
+
+/*
+ * Group the T*K routed slots (slot s = t*K + k) by expert.
+ *
+ *   ids         [T][K] int32, each in [0, E)   (in)
+ *   counts      [E'] int32        (out) slots per group; counts[E] = T if shared
+ *   offsets     [E'+1] int32      (out) exclusive prefix sum of counts
+ *   sorted_slot [T*K + T*has_shared] int32 (out) slots grouped by expert, in
+ *               ascending slot order inside each group; the shared group is
+ *               slots T*K + t for t = 0..T-1 in token order, at positions
+ *               offsets[E] + t (offsets[E] = T*K when every id is valid)
+ *   slot_pos    [T*K + T*has_shared] int32 (out) position of slot s in
+ *               sorted_slot, for the routed and the shared slots (the inverse)
+ *   ws          device workspace of at least
+ *               moe_workspace_bytes(MOE_OP_PERMUTE, T, E, K, 0, 0, has_shared, 0)
+ *
+ * A slot whose id is outside [0, E) belongs to no group: it is not counted and
+ * its slot_pos is -1 (later stages skip it).  The order never depends on
+ * timing: positions are computed from counts, not from atomics.
+ */
+int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFN of every group on the rows routed to it.  For the row of sorted
+ * position p in group e (token t = sorted_slot[p] / K, or sorted_slot[p] - T*K
+ * in the shared group):
+ *
+ *   g = x[t] . W_gate,e^T,  u = x[t] . W_up,e^T          (f32 accumulate)
+ *   h = bf16( silu(g) * u ),  silu(g) = g / (1 + exp(-g))
+ *   y_slots[p] = bf16( h . W_down,e^T )
+ *
+ * with W the dequantised NVFP4 weights (scale2 applied to the f32 sums).
+ * With act_mode MOE_ACT_FP8_ROW the gate_up input is instead the e4m3 row
+ * quantisation of x: s_t = absmax(x[t]) / 448, q = e4m3_rne_sat(x[t] * (448 /
+ * absmax)), and s_t multiplies the f32 sums of g and u (option (a) of the
+ * issue above; weights stay exact, the product runs on bf16 MFMA).
+ *
+ *   W        host struct of device pointers, see moe_nvfp4_weights
+ *   x        [T][H] bf16 bit patterns                (in)
+ *   offsets  [E'+1], sorted_slot [T*K + T*has_shared] from moe_permute (in)
+ *   y_slots  [T*K + T*has_shared][H] bf16            (out) by sorted position
+ *   ws       device workspace of at least
+ *            moe_workspace_bytes(MOE_OP_EXPERT_FFN, T, E, K, H, I, has_shared, act_mode)
+ *
+ * T <= 8 runs the decode path (multi-row GEMV streaming each active expert's
+ * weights once), larger T the grouped-GEMM path; both compute the same
+ * function.  Rows whose sorted_slot entry is out of range are skipped.
+ *
+ * Workspace contents after the call (S = T*K + T*has_shared, A(n) = n rounded
+ * up to a multiple of 256): bytes [0, 2*S*I) hold h as bf16 [S][I] by sorted
+ * position; with MOE_ACT_FP8_ROW the e4m3 codes [T][H] follow at byte
+ * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).
+ */
+int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
+                   const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
+                   uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine: out[t] = bf16( sum_{k=0..K-1} w[t][k] * y_slots[slot_pos[t*K+k]]
+ *                          + y_slots[slot_pos[T*K + t]] (if has_shared) ),
+ * accumulated in fp32 in exactly this order (slot order, then the shared
+ * expert) with one round-to-nearest-even at the end, so the result does not
+ * depend on how the work is split (the same-order rule of the issue "EXL3
+ * Qwen3.8-Flash-Next on CUDA sm_120 ...", expert-parallel TP=2).
+ *
+ *   y_slots [T*K + T*has_shared][H] bf16, w [T][K] float32,
+ *   slot_pos [T*K + T*has_shared] int32 from moe_permute  (in)
+ *   out     [T][H] bf16 bit patterns  (out)
+ *
+ * Routed slots with slot_pos outside [0, T*K) and a shared slot outside
+ * [0, T*K + T) are skipped.  H must be a multiple of 8.
+ */
+int moe_combine(const uint16_t* y_slots, const float* w, const int32_t* slot_pos, int T, int K,
+                int H, int has_shared, uint16_t* out, void* stream);
+
+/*
+ * Per-kernel timing, for measurement only.  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on its stream (so
+ * do not enable it while capturing a graph).  moe_timing_read() waits for the
+ * recorded events and reports, for each kernel name launched since the last
+ * reset, the number of launches and their summed duration in milliseconds.
+ * At most 65536 launches are recorded between resets; later ones are counted
+ * in `dropped`.  Returns the number of names written (<= max_names), or a
+ * negative status.  Names are static strings owned by the library.
+ */
+int moe_timing_enable(int on);
+int moe_timing_reset(void);
+int moe_timing_read(const char** names, int* launches, double* total_ms, int max_names,
+                    int* dropped);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

@@ -97,12 +97,13 @@ def expert_outputs(xin: np.ndarray, bank, T: int, K: int, offsets, sorted_slot,
 
 def combine(y_slots: np.ndarray, w: np.ndarray, slot_pos: np.ndarray, T: int, K: int,
             has_shared: bool) -> np.ndarray:
-    sp = np.asarray(slot_pos, dtype=np.int64).reshape(T, K)
+    sp_all = np.asarray(slot_pos, dtype=np.int64)
+    sp = sp_all[:T * K].reshape(T, K)
     out = np.zeros((T, y_slots.shape[1]), dtype=np.float64)
     for k in range(K):
         out += w[:, k:k + 1] * y_slots[sp[:, k]]
     if has_shared:
-        out += y_slots[T * K + np.arange(T)]
+        out += y_slots[sp_all[T * K:T * K + T]]
     return out
 
 

@@ -11,7 +11,9 @@ layer asks for a bit-exact permutation):
   inside each group (reading: the pages fix no order inside a group; ascending
   is the stable choice and equals ascending token); the shared group follows as
   slots T*K + t for t = 0 .. T-1;
-* slot_pos[s] = position of routed slot s in sorted_slot (the inverse).
+* slot_pos[s] = position of slot s in sorted_slot, for the routed slots and,
+  with a shared expert, for the shared slots T*K + t as well (the inverse of
+  sorted_slot over every slot; the shared group starts at offsets[E]).
 
 Pins: pure-Python loops on random, skewed and empty-expert cases.
 """
@@ -34,7 +36,9 @@ def permute(ids: np.ndarray, E: int, has_shared: bool):
     sorted_slot = order
     if has_shared:
         sorted_slot = np.concatenate([order, T * K + np.arange(T)])
-    slot_pos = np.empty(T * K, dtype=np.int64)
+    slot_pos = np.empty(T * K + (T if has_shared else 0), dtype=np.int64)
     slot_pos[order] = np.arange(T * K)
+    if has_shared:
+        slot_pos[T * K:] = offsets[E] + np.arange(T)
     return (counts.astype(np.int32), offsets, sorted_slot.astype(np.int32),
             slot_pos.astype(np.int32))

@@ -1,0 +1,70 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (no GPU needed: argument errors return before any HIP
+call)."""
+import ctypes
+
+import pytest
+
+from _libutil import declared_functions, ensure_built
+
+
+@pytest.fixture(scope="module")
+def lib():
+    ensure_built()
+    from bit_block_quantized_nvfp4_amd import _lib
+
+    return _lib.lib()
+
+
+def test_header_declares_the_four_layer_calls():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_init",
+              "moe_last_error", "moe_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(lib._name)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+
+
+def test_argument_errors_are_reported_without_a_gpu(lib):
+    from bit_block_quantized_nvfp4_amd import _lib as L
+
+    P = ctypes.c_void_p
+    one = P(16)
+    assert lib.moe_route_topk(None, 4, 8, 2, one, one, None) == L.MOE_EINVAL
+    assert b"null" in lib.moe_last_error()
+    assert lib.moe_route_topk(one, 4, 8, 9, one, one, None) == L.MOE_EINVAL     # K > E
+    assert lib.moe_route_topk(one, 4, 2048, 2, one, one, None) == L.MOE_EINVAL  # E > 1024
+    assert lib.moe_route_topk(one, 4, 64, 33, one, one, None) == L.MOE_EINVAL   # K > 32
+    assert lib.moe_route_topk(one, 0, 8, 2, one, one, None) == L.MOE_EINVAL     # T < 1
+    assert lib.moe_permute(one, 4, 8, 2, 2, one, one, one, one, None, 0, None) == L.MOE_EINVAL
+    # a large permute needs a workspace
+    assert lib.moe_permute(one, 4096, 512, 10, 1, one, one, one, one, None, 0, None) == L.MOE_EWORKSPACE
+    W = L.MoeNvfp4Weights(16, 16, 16, 16, 16, 8, 256, 128, 0)
+    ffn = lib.moe_expert_ffn
+    assert ffn(ctypes.byref(W), one, 4, 2, one, one, 7, one, one, 1 << 20, None) == L.MOE_EUNSUPPORTED
+    bad = L.MoeNvfp4Weights(16, 16, 16, 16, 16, 8, 200, 128, 0)   # H not a multiple of 256
+    assert ffn(ctypes.byref(bad), one, 4, 2, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
+    assert ffn(ctypes.byref(W), one, 4, 2, one, one, 0, one, one, 16, None) == L.MOE_EWORKSPACE
+    nullw = L.MoeNvfp4Weights(0, 16, 16, 16, 16, 8, 256, 128, 0)
+    assert ffn(ctypes.byref(nullw), one, 4, 2, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
+    assert lib.moe_combine(one, one, one, 4, 2, 12, 0, one, None) == L.MOE_EINVAL  # H % 8
+    assert lib.moe_combine(one, one, None, 4, 2, 16, 0, one, None) == L.MOE_EINVAL
+
+
+def test_workspace_sizes(lib):
+    from bit_block_quantized_nvfp4_amd import _lib as L
+
+    ws = lib.moe_workspace_bytes
+    # the decode permutation runs in one workgroup without a workspace
+    assert ws(L.MOE_OP_PERMUTE, 8, 512, 10, 0, 0, 1, 0) == 0
+    assert ws(L.MOE_OP_PERMUTE, 4096, 512, 10, 0, 0, 1, 0) > 0
+    S = 4096 * 10 + 4096
+    bf = ws(L.MOE_OP_EXPERT_FFN, 4096, 512, 10, 2048, 512, 1, L.MOE_ACT_BF16)
+    fp8 = ws(L.MOE_OP_EXPERT_FFN, 4096, 512, 10, 2048, 512, 1, L.MOE_ACT_FP8_ROW)
+    assert bf >= S * 512 * 2 and fp8 >= bf + 4096 * 2048 + 4096 * 4
+    assert ws(L.MOE_OP_EXPERT_FFN, 4096, 512, 10, 2048, 512, 1, 9) == 0
+    assert ws(99, 4, 8, 2, 256, 128, 0, 0) == 0

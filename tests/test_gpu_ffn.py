@@ -1,0 +1,214 @@
+"""GPU parity of the expert FFN (A3-A9) and the combine (A10) against the fp64
+oracle.
+
+Gates (north-star reading of "max relative error", normwise over the whole
+output: max|y - y_ref| / max|y_ref|):
+  * bf16 path vs the exact fp64 oracle:                    <= 2e-2
+  * FP8-activation arm vs the exact fp64 oracle:           <= 6e-2
+  * either path vs the oracle that rounds h and the per-slot outputs to bf16
+    where the GPU stores bf16 (and quantises x in the FP8 arm): <= 8e-3,
+    tight enough to catch a wrong block scale or a dropped term.
+Derivation of the bounds: h and y are stored in bf16 (relative rounding
+2^-9 each) and the output is rounded once more, so the bf16 path sits near
+3 x 2^-9 ~ 6e-3 normwise in the worst element; f32 accumulation over K <= 2048
+adds ~1e-6.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import bf16_np, flush, normwise, setup, x_dev
+from oracle.ffn import bf16_bits_to_f64
+from workloads import DECODE_TS, make_workload, workload_for
+
+pytestmark = pytest.mark.gpu
+
+GATE_BF16, GATE_FP8, GATE_TIGHT = 2e-2, 6e-2, 8e-3
+
+
+@pytest.fixture(scope="module")
+def moe():
+    return setup()
+
+
+def _run(moe, wl, act_mode=0, W=None):
+    W = W or moe.NVFP4Weights.from_bank(wl.weights)
+    r = moe.moe_layer(W, x_dev(wl.x_bf16), torch.from_numpy(wl.logits).cuda(), wl.K, act_mode)
+    torch.cuda.synchronize()
+    return r
+
+
+def _full_check(moe, wl, act_mode=0, tag=""):
+    r = _run(moe, wl, act_mode)
+    om = "fp8_row" if act_mode else "bf16"
+    exact = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
+    emul = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K, act_mode=om,
+                            h_round="bf16", y_round="bf16")
+    # integer stages bit-exact
+    assert np.array_equal(r["ids"].cpu().numpy(), exact["ids"])
+    assert np.array_equal(r["sorted_slot"].cpu().numpy(), exact["sorted_slot"])
+    y = bf16_np(r["y_slots"])
+    out = bf16_np(r["out"])
+    e_y = normwise(y, emul["y_slots"])
+    e_tight = normwise(out, emul["out"])
+    e_exact = normwise(out, exact["out"])
+    flush(f"{tag} act={om}: y vs emul {e_y:.2e}  out vs emul {e_tight:.2e}  out vs exact {e_exact:.2e}")
+    assert e_y <= GATE_TIGHT
+    assert e_tight <= GATE_TIGHT
+    assert e_exact <= (GATE_FP8 if act_mode else GATE_BF16)
+    # combine on the GPU's own per-slot outputs and weights, fp64, within one bf16 rounding
+    ref = oracle.combine(y, r["w"].cpu().numpy().astype(np.float64), r["slot_pos"].cpu().numpy(),
+                         wl.T, wl.K, wl.has_shared)
+    mag = np.max(np.abs(ref), axis=1, keepdims=True)
+    assert np.all(np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * mag)
+    return r
+
+
+def test_tiny_layer(moe):
+    _full_check(moe, workload_for("tiny"), tag="tiny")
+
+
+@pytest.mark.parametrize("T", DECODE_TS)
+def test_decode_layer_full_size(moe, T):
+    _full_check(moe, workload_for("decode", T=T), tag=f"decode T={T}")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=300, H=2048, E=64, K=10, I=512, has_shared=True),     # ragged tiles, H=2048
+    dict(T=700, H=256, E=4, K=2, I=128, has_shared=True),        # several 128-row tiles per expert
+    dict(T=9, H=512, E=16, K=4, I=256, has_shared=False),        # just above the decode switch
+    dict(T=64, H=1024, E=512, K=10, I=384, has_shared=True),     # many empty experts, I % 256 != 0
+])
+def test_grouped_path_medium(moe, cfg):
+    wl = make_workload("m", seed=3, **cfg)
+    _full_check(moe, wl, tag=f"grouped {cfg}")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=4, H=256, E=8, K=2, I=128, has_shared=False),
+    dict(T=8, H=2048, E=512, K=10, I=512, has_shared=True),
+    dict(T=300, H=2048, E=64, K=10, I=512, has_shared=True),
+])
+def test_fp8_arm(moe, cfg):
+    wl = make_workload("f", seed=4, x_kind="student_t", **cfg)
+    r = _full_check(moe, wl, act_mode=1, tag=f"fp8 {cfg}")
+    # the row quantisation itself is bit-exact: codes and scales sit in the workspace
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    _, ws = moe.moe_expert_ffn(W, x_dev(wl.x_bf16), wl.K, r["offsets"], r["sorted_slot"], 1,
+                               return_ws=True)
+    torch.cuda.synchronize()
+    S = wl.T * wl.K + (wl.T if wl.has_shared else 0)
+    off = (S * wl.I * 2 + 255) // 256 * 256
+    q = ws[off:off + wl.T * wl.H].cpu().numpy().reshape(wl.T, wl.H)
+    off2 = off + (wl.T * wl.H + 255) // 256 * 256
+    s = ws[off2:off2 + 4 * wl.T].cpu().numpy().view(np.float32)
+    qo, so = oracle.rowquant_e4m3(bf16_bits_to_f64(wl.x_bf16).astype(np.float32))
+    assert np.array_equal(s, so)
+    assert np.array_equal(q, qo)
+
+
+def test_fp8_zero_rows(moe):
+    wl = make_workload("z", T=12, H=256, E=8, K=2, I=128, has_shared=True, seed=6)
+    wl.x_bf16[3] = 0
+    wl.x_bf16[7] = 0x8000          # -0.0
+    _full_check(moe, wl, act_mode=1, tag="fp8 zero rows")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=5, H=256, E=8, K=1, I=128, has_shared=False),
+    dict(T=20, H=256, E=8, K=8, I=128, has_shared=False),
+    dict(T=1, H=256, E=1, K=1, I=128, has_shared=True),
+    dict(T=33, H=256, E=8, K=1, I=128, has_shared=True),
+])
+def test_degenerate_routing(moe, cfg):
+    _full_check(moe, make_workload("d", seed=7, **cfg), tag=f"degenerate {cfg}")
+
+
+def test_scale2_is_applied(moe):
+    wl = make_workload("s", T=40, H=256, E=8, K=2, I=128, has_shared=True, seed=8)
+    rng = np.random.default_rng(0)
+    wl.weights.scale2[:] = rng.uniform(0.25, 3.0, wl.weights.scale2.shape).astype(np.float32)
+    _full_check(moe, wl, tag="scale2")
+    wl2 = make_workload("s", T=6, H=256, E=8, K=2, I=128, has_shared=True, seed=8)
+    wl2.weights.scale2[:] = wl.weights.scale2
+    _full_check(moe, wl2, tag="scale2 decode")
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_token_permutation_is_bitwise_equivariant(moe, name):
+    wl = workload_for(name, T=8 if name == "decode" else 512)
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    a = _run(moe, wl, W=W)["out"]
+    p = np.random.default_rng(1).permutation(wl.T)
+    wl.x_bf16 = np.ascontiguousarray(wl.x_bf16[p])
+    wl.logits = np.ascontiguousarray(wl.logits[p])
+    b = _run(moe, wl, W=W)["out"]
+    assert torch.equal(a[torch.from_numpy(p).cuda()].view(torch.int16), b.view(torch.int16))
+
+
+def test_repeated_layer_calls_are_bitwise_identical(moe):
+    wl = workload_for("prefill", T=1024)
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    a = _run(moe, wl, W=W)
+    b = _run(moe, wl, W=W)
+    for k in ("y_slots", "out"):
+        assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16))
+
+
+def _sampled_check(moe, name, act_mode=0, n_tok=6):
+    """Full-size run; the oracle recomputes only a sample of tokens (all their
+    routed experts and the shared expert) and the per-slot outputs of those tokens."""
+    wl = workload_for(name)
+    flush(f"sampled {name} T={wl.T} act={act_mode}")
+    r = _run(moe, wl, act_mode)
+    ids = r["ids"].cpu().numpy()
+    ids_o, w_o = oracle.route_topk(wl.logits, wl.K)
+    assert np.array_equal(ids, ids_o)
+    slot_pos = r["slot_pos"].cpu().numpy()
+    rng = np.random.default_rng(11)
+    toks = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, n_tok, replace=False)]))
+    x = bf16_np(x_dev(wl.x_bf16)[torch.from_numpy(toks).cuda()])
+    if act_mode:
+        xq = oracle.rowquant_dequant(x.astype(np.float32))
+    y_gpu = r["y_slots"]
+    cache = {}
+
+    def ffn(e, rows, h_round):
+        if e not in cache:
+            cache[e] = oracle.ffn.dequant_expert(wl.weights, e)
+        return oracle.expert_ffn(rows, *cache[e], h_round=h_round)
+
+    out_gpu = bf16_np(r["out"][torch.from_numpy(toks).cuda()])
+    worst_y = 0.0
+    out_ref = np.zeros_like(out_gpu)
+    for i, t in enumerate(toks):
+        xin = xq[i:i + 1] if act_mode else x[i:i + 1]
+        for k in range(wl.K):
+            e = int(ids[t, k])
+            yk = ffn(e, xin, "none")[0]
+            ye = ffn(e, xin, "bf16")[0]
+            yg = bf16_np(y_gpu[int(slot_pos[t * wl.K + k])])
+            worst_y = max(worst_y, normwise(yg, ye))
+            out_ref[i] += w_o[t, k] * yk
+        ys = ffn(wl.E, x[i:i + 1], "none")[0]  # shared expert: same input arm
+        if act_mode:
+            ys = ffn(wl.E, xin, "none")[0]
+        out_ref[i] += ys
+    e_out = normwise(out_gpu, out_ref)
+    flush(f"  sampled {len(toks)} tokens: worst y vs emul {worst_y:.2e}  out vs oracle {e_out:.2e}")
+    assert worst_y <= GATE_TIGHT
+    assert e_out <= (GATE_TIGHT if not act_mode else GATE_FP8)
+
+
+def test_prefill_full_size_sampled(moe):
+    _sampled_check(moe, "prefill")
+
+
+def test_long_prefill_full_size_sampled(moe):
+    _sampled_check(moe, "long_prefill")
+
+
+def test_fp8_arm_full_size_sampled(moe):
+    _sampled_check(moe, "fp8_arm", act_mode=1)
+    _sampled_check(moe, "fp8_arm", act_mode=0)

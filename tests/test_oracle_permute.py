@@ -18,10 +18,9 @@ def _brute(ids, E, has_shared):
     for c in counts:
         offsets.append(offsets[-1] + c)
     sorted_slot = [s for g in groups for s in g]
-    slot_pos = [None] * (T * K)
+    slot_pos = [None] * (T * K + (T if has_shared else 0))
     for p, s in enumerate(sorted_slot):
-        if s < T * K:
-            slot_pos[s] = p
+        slot_pos[s] = p
     return counts, offsets, sorted_slot, slot_pos
 
 

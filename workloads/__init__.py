@@ -7,6 +7,7 @@ can take their inputs from it without sharing any of the method.
 """
 from .generators import (  # noqa: F401
     CONFIGS,
+    DECODE_TS,
     MoEWorkload,
     WeightBank,
     make_weights,
