@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 routed-MoE layer on one MI355X.
+
+A step is one whole layer call -- moe_route_topk, moe_permute, moe_expert_ffn
+(gate_up + SiLU + down, routed experts and the shared expert), moe_combine --
+over one batch of synthetic tokens already resident in HBM.
+
+Headline workload: the decode/verify layer at T=8 rows (H=2048, 512 experts
+top-10 plus one shared expert, I=512).  Every step uses the next of NBANKS
+device copies of the 907.7 MB weight bank and the next of NLOGITS router-logit
+sets, so no step finds its experts in the 256 MB Infinity Cache left by the
+one before.  The same loop is then run at T=1, 2, 4 and on the prefill chunk
+(T=4096) as extra lines of the report.
+
+Per-kernel durations come from HIP events that the library records around each
+of its launches on the launch stream (moe_timing_*), in a second pass of the
+same steps right after the timed pass.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+NBANKS = 8
+NLOGITS = 16
+
+
+def _gate_up_bytes(H, I):
+    return 2 * I * H // 2 + 2 * I * H // 16
+
+
+def _down_bytes(H, I):
+    return H * I // 2 + H * I // 16
+
+
+class LayerRunner:
+    """Pre-allocated buffers for one workload; run(step) enqueues one layer call."""
+
+    def __init__(self, moe, torch, banks, wl, logits_sets, act_mode=0):
+        self.moe, self.torch = moe, torch
+        self.banks, self.wl, self.act_mode = banks, wl, act_mode
+        dev = "cuda"
+        T, K, E, H = wl.T, wl.K, wl.E, wl.H
+        hs = wl.has_shared
+        S = T * K + (T if hs else 0)
+        self.x = torch.from_numpy(wl.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.logits = [torch.from_numpy(l).to(dev) for l in logits_sets]
+        i32 = torch.int32
+        self.ids = torch.empty((T, K), dtype=i32, device=dev)
+        self.w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        G = E + int(hs)
+        self.perm = (torch.empty(G, dtype=i32, device=dev), torch.empty(G + 1, dtype=i32, device=dev),
+                     torch.empty(S, dtype=i32, device=dev), torch.empty(S, dtype=i32, device=dev))
+        self.ws_p = torch.empty(max(1, moe.workspace_bytes(1, T, E, K, 0, 0, hs)), dtype=torch.uint8,
+                                device=dev)
+        self.ws_f = torch.empty(moe.workspace_bytes(2, T, E, K, H, wl.I, hs, act_mode),
+                                dtype=torch.uint8, device=dev)
+        self.y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.distinct = []
+
+    def run(self, step):
+        moe = self.moe
+        W = self.banks[step % len(self.banks)]
+        lg = self.logits[step % len(self.logits)]
+        moe.moe_route_topk(lg, self.wl.K, self.ids, self.w)
+        moe.moe_permute(self.ids, self.wl.E, self.wl.has_shared, self.ws_p, self.perm)
+        moe.moe_expert_ffn(W, self.x, self.wl.K, self.perm[1], self.perm[2], self.act_mode,
+                           self.ws_f, self.y)
+        moe.moe_combine(self.y, self.w, self.perm[3], self.wl.K, self.wl.has_shared, self.out)
+
+    def active_groups(self):
+        """Distinct active groups per logits set (from the GPU's own counts)."""
+        res = []
+        for i in range(len(self.logits)):
+            self.run(i)
+            self.torch.cuda.synchronize()
+            res.append(int((self.perm[0] > 0).sum().item()))
+        return res
+
+
+def time_steps(runner, torch, steps, warmup):
+    for i in range(warmup):
+        runner.run(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(steps):
+        runner.run(warmup + i)
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall
+
+
+def kernel_times(runner, torch, moe_ops, steps, warmup):
+    moe_ops.timing_reset()
+    moe_ops.timing_enable(True)
+    for i in range(steps):
+        runner.run(warmup + i)
+    torch.cuda.synchronize()
+    moe_ops.timing_enable(False)
+    res = moe_ops.timing_read()
+    moe_ops.timing_reset()
+    return {k: {"launches": n, "avg_us": 1000.0 * ms / max(n, 1)} for k, (n, ms) in res.items()}
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle on the host cores, on repeated calls of the same layer."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n * wl.T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} fp64 oracle calls of the T={wl.T} layer (same workload, same bank), "
+                      f"{dt:.1f} s, numpy BLAS threads = host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="skip the T=1,2,4 and prefill lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the expert-parallel split is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_block_quantized_nvfp4_amd as moe
+    from bit_block_quantized_nvfp4_amd import ops as moe_ops
+    from workloads import CONFIGS, make_workload, workload_for
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    moe.moe_init()
+    dev_name = torch.cuda.get_device_name(0)
+    print(f"# device {dev_name}", file=sys.stderr, flush=True)
+
+    base = workload_for("decode", T=8)
+    bank0 = moe.NVFP4Weights.from_bank(base.weights)
+    banks = [bank0]
+    for _ in range(NBANKS - 1):
+        banks.append(moe.NVFP4Weights(bank0.gu_codes.clone(), bank0.gu_scales.clone(),
+                                      bank0.dn_codes.clone(), bank0.dn_scales.clone(),
+                                      bank0.scale2.clone(), bank0.E, bank0.H, bank0.I,
+                                      bank0.has_shared))
+    torch.cuda.synchronize()
+    H, I = base.H, base.I
+    print(f"# {NBANKS} weight banks of {base.weights.bytes_per_expert * (base.E + 1) / 1e6:.1f} MB",
+          file=sys.stderr, flush=True)
+
+    def decode_line(T, steps, warmup):
+        wl = workload_for("decode", T=T, with_weights=False)
+        wl.weights = base.weights
+        lsets = [workload_for("decode", T=T, seed=s, with_weights=False).logits for s in range(NLOGITS)]
+        r = LayerRunner(moe, torch, banks, wl, lsets)
+        ms, wall = time_steps(r, torch, steps, warmup)
+        kt = kernel_times(r, torch, moe_ops, steps, warmup)
+        act = r.active_groups()
+        n_act = float(np.mean(act))
+        S = T * wl.K + T
+        gu_bytes = n_act * _gate_up_bytes(H, I) + T * H * 2 + S * I * 2
+        dn_bytes = n_act * _down_bytes(H, I) + S * I * 2 + S * H * 2
+        layer_bytes = (n_act * (_gate_up_bytes(H, I) + _down_bytes(H, I)) + 2 * T * H * 2
+                       + T * wl.E * 4)
+        gu = kt.get("gemv_gate_up", {"avg_us": float("nan")})
+        dn = kt.get("gemv_down", {"avg_us": float("nan")})
+        return dict(T=T, ms_per_step=ms, wall_s=wall, tokens_per_s=T / (ms / 1e3),
+                    active_groups=n_act, layer_bytes=layer_bytes,
+                    layer_GBs=layer_bytes / (ms / 1e3) / 1e9, kernels=kt,
+                    gate_up=dict(bytes=gu_bytes, avg_us=gu["avg_us"],
+                                 GBs=gu_bytes / (gu["avg_us"] * 1e-6) / 1e9),
+                    down=dict(bytes=dn_bytes, avg_us=dn["avg_us"],
+                              GBs=dn_bytes / (dn["avg_us"] * 1e-6) / 1e9))
+
+    head = decode_line(8, args.steps, args.warmup)
+    print(f"# decode T=8: {head['ms_per_step'] * 1e3:.1f} us/layer, gate_up "
+          f"{head['gate_up']['avg_us']:.1f} us {head['gate_up']['GBs']:.0f} GB/s, kernels {head['kernels']}",
+          file=sys.stderr, flush=True)
+
+    extra = {}
+    if not args.no_extra:
+        for T in (1, 2, 4):
+            d = decode_line(T, args.steps, args.warmup)
+            extra[f"decode_T{T}"] = {
+                "tokens_per_s": round(d["tokens_per_s"], 1), "us_per_layer": round(d["ms_per_step"] * 1e3, 2),
+                "layer_GBs": round(d["layer_GBs"], 1),
+                "gate_up": {"avg_us": round(d["gate_up"]["avg_us"], 2), "GBs": round(d["gate_up"]["GBs"], 1),
+                            "frac": round(d["gate_up"]["GBs"] / HBM_PEAK_GBS, 4)},
+                "down": {"avg_us": round(d["down"]["avg_us"], 2), "GBs": round(d["down"]["GBs"], 1)},
+                "kernels": {k: round(v["avg_us"], 2) for k, v in d["kernels"].items()}}
+            print(f"# decode T={T}: {d['ms_per_step'] * 1e3:.1f} us/layer", file=sys.stderr, flush=True)
+        for name in ("prefill",):
+            wl = workload_for(name, with_weights=False)
+            wl.weights = base.weights
+            lsets = [workload_for(name, seed=s, with_weights=False).logits for s in range(2)]
+            r = LayerRunner(moe, torch, banks, wl, lsets)
+            ms, _ = time_steps(r, torch, args.prefill_steps, 2)
+            kt = kernel_times(r, torch, moe_ops, args.prefill_steps, 2)
+            S = wl.T * wl.K + wl.T
+            fl_gu = 2.0 * S * H * 2 * I
+            fl_dn = 2.0 * S * I * H
+            gu, dn = kt["grouped_gate_up"]["avg_us"], kt["grouped_down"]["avg_us"]
+            extra[name + f"_T{wl.T}"] = {
+                "tokens_per_s": round(wl.T / (ms / 1e3), 1), "us_per_layer": round(ms * 1e3, 1),
+                "layer_TFLOPs": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12, 1),
+                "grouped_gate_up": {"avg_us": round(gu, 1), "TFLOPs": round(fl_gu / (gu * 1e-6) / 1e12, 1),
+                                    "frac": round(fl_gu / (gu * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                "grouped_down": {"avg_us": round(dn, 1), "TFLOPs": round(fl_dn / (dn * 1e-6) / 1e12, 1),
+                                 "frac": round(fl_dn / (dn * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                "kernels": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+            print(f"# {name}: {ms * 1e3:.1f} us/layer, kernels {kt}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        wl = workload_for("decode", T=8, with_weights=False)
+        wl.weights = base.weights
+        cpu = cpu_baseline(wl)
+        print(f"# cpu baseline {cpu}", file=sys.stderr, flush=True)
+
+    gu = head["gate_up"]
+    line = {
+        "metric": "MoE-layer tokens/s (decode/verify layer)",
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode/verify MoE layer: T=8 rows, H=2048, 512 routed experts top-10 "
+                               "+ 1 shared, I=512, NVFP4 weights (e2m1, e4m3 per 16, fp32 scale2), "
+                               "bf16 activations; 8 rotating weight banks",
+                   "global_batch": 8, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "gemv_gate_up", "achieved": round(gu["GBs"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_us": round(gu["avg_us"], 2),
+                     "bytes_per_launch": int(gu["bytes"])},
+        "cpu_baseline": cpu,
+        "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "GBs": round(head["layer_GBs"], 1),
+                  "frac": round(head["layer_GBs"] / HBM_PEAK_GBS, 4),
+                  "active_groups": round(head["active_groups"], 2),
+                  "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in head["kernels"].items()},
+                  "down": {"avg_us": round(head["down"]["avg_us"], 2),
+                           "GBs": round(head["down"]["GBs"], 1)}},
+        "extra": extra,
+        "device": dev_name,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
