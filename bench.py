@@ -12,9 +12,11 @@ sets, so no step finds its experts in the 256 MB Infinity Cache left by the
 one before.  The same loop is then run at T=1, 2, 4 and on the prefill chunk
 (T=4096) as extra lines of the report.
 
-Per-kernel durations come from HIP events that the library records around each
-of its launches on the launch stream (moe_timing_*), in a second pass of the
-same steps right after the timed pass.
+The timed steps are captured once into a HIP graph and replayed, so the time
+is the GPU's (the library's entry points are capturable); the eager time of
+the same steps is reported beside it.  Per-kernel durations come from HIP
+events that the library records around each of its launches on the launch
+stream (moe_timing_*), in an eager pass of the same steps right after.
 """
 from __future__ import annotations
 
@@ -60,7 +62,8 @@ class LayerRunner:
         self.w = torch.empty((T, K), dtype=torch.float32, device=dev)
         G = E + int(hs)
         self.perm = (torch.empty(G, dtype=i32, device=dev), torch.empty(G + 1, dtype=i32, device=dev),
-                     torch.empty(S, dtype=i32, device=dev), torch.empty(S, dtype=i32, device=dev))
+                     torch.empty(S, dtype=i32, device=dev), torch.empty(S, dtype=i32, device=dev),
+                     torch.empty(G + 1, dtype=i32, device=dev))
         self.ws_p = torch.empty(max(1, moe.workspace_bytes(1, T, E, K, 0, 0, hs)), dtype=torch.uint8,
                                 device=dev)
         self.ws_f = torch.empty(moe.workspace_bytes(2, T, E, K, H, wl.I, hs, act_mode),
@@ -75,8 +78,8 @@ class LayerRunner:
         lg = self.logits[step % len(self.logits)]
         moe.moe_route_topk(lg, self.wl.K, self.ids, self.w)
         moe.moe_permute(self.ids, self.wl.E, self.wl.has_shared, self.ws_p, self.perm)
-        moe.moe_expert_ffn(W, self.x, self.wl.K, self.perm[1], self.perm[2], self.act_mode,
-                           self.ws_f, self.y)
+        moe.moe_expert_ffn(W, self.x, self.wl.K, self.perm[1], self.perm[2], self.perm[4],
+                           self.act_mode, self.ws_f, self.y)
         moe.moe_combine(self.y, self.w, self.perm[3], self.wl.K, self.wl.has_shared, self.out)
 
     def active_groups(self):
@@ -89,15 +92,33 @@ class LayerRunner:
         return res
 
 
-def time_steps(runner, torch, steps, warmup):
+def time_steps(runner, torch, steps, warmup, graph=True):
+    """ms per step over exactly `steps` layer calls.
+
+    With graph=True the `steps` calls are captured once into a HIP graph
+    (every library entry point is capturable: no allocation, no sync, no
+    memset) and the graph is replayed: the time is the GPU's, not the Python
+    launch path's.  Eager mode times the same calls launched one by one.
+    """
     for i in range(warmup):
         runner.run(i)
     torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                runner.run(warmup + i)
+        g.replay()                      # untimed replay
+        torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     a.record()
-    for i in range(steps):
-        runner.run(warmup + i)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            runner.run(warmup + i)
     b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -179,7 +200,8 @@ def main():
         wl.weights = base.weights
         lsets = [workload_for("decode", T=T, seed=s, with_weights=False).logits for s in range(NLOGITS)]
         r = LayerRunner(moe, torch, banks, wl, lsets)
-        ms, wall = time_steps(r, torch, steps, warmup)
+        ms, wall = time_steps(r, torch, steps, warmup, graph=True)
+        ms_eager, _ = time_steps(r, torch, steps, warmup, graph=False)
         kt = kernel_times(r, torch, moe_ops, steps, warmup)
         act = r.active_groups()
         n_act = float(np.mean(act))
@@ -188,9 +210,9 @@ def main():
         dn_bytes = n_act * _down_bytes(H, I) + S * I * 2 + S * H * 2
         layer_bytes = (n_act * (_gate_up_bytes(H, I) + _down_bytes(H, I)) + 2 * T * H * 2
                        + T * wl.E * 4)
-        gu = kt.get("gemv_gate_up", {"avg_us": float("nan")})
-        dn = kt.get("gemv_down", {"avg_us": float("nan")})
-        return dict(T=T, ms_per_step=ms, wall_s=wall, tokens_per_s=T / (ms / 1e3),
+        gu = kt["dec_gate_up"]
+        dn = kt["dec_down"]
+        return dict(T=T, ms_per_step=ms, ms_eager=ms_eager, wall_s=wall, tokens_per_s=T / (ms / 1e3),
                     active_groups=n_act, layer_bytes=layer_bytes,
                     layer_GBs=layer_bytes / (ms / 1e3) / 1e9, kernels=kt,
                     gate_up=dict(bytes=gu_bytes, avg_us=gu["avg_us"],
@@ -209,6 +231,7 @@ def main():
             d = decode_line(T, args.steps, args.warmup)
             extra[f"decode_T{T}"] = {
                 "tokens_per_s": round(d["tokens_per_s"], 1), "us_per_layer": round(d["ms_per_step"] * 1e3, 2),
+                "us_per_layer_eager": round(d["ms_eager"] * 1e3, 2),
                 "layer_GBs": round(d["layer_GBs"], 1),
                 "gate_up": {"avg_us": round(d["gate_up"]["avg_us"], 2), "GBs": round(d["gate_up"]["GBs"], 1),
                             "frac": round(d["gate_up"]["GBs"] / HBM_PEAK_GBS, 4)},
@@ -220,7 +243,7 @@ def main():
             wl.weights = base.weights
             lsets = [workload_for(name, seed=s, with_weights=False).logits for s in range(2)]
             r = LayerRunner(moe, torch, banks, wl, lsets)
-            ms, _ = time_steps(r, torch, args.prefill_steps, 2)
+            ms, _ = time_steps(r, torch, args.prefill_steps, 2, graph=True)
             kt = kernel_times(r, torch, moe_ops, args.prefill_steps, 2)
             S = wl.T * wl.K + wl.T
             fl_gu = 2.0 * S * H * 2 * I
@@ -261,12 +284,14 @@ def main():
                                "+ 1 shared, I=512, NVFP4 weights (e2m1, e4m3 per 16, fp32 scale2), "
                                "bf16 activations; 8 rotating weight banks",
                    "global_batch": 8, "seq_len": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "gemv_gate_up", "achieved": round(gu["GBs"], 1),
+        "roofline": {"bound": "hbm", "kernel": "dec_gate_up", "achieved": round(gu["GBs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_us": round(gu["avg_us"], 2),
                      "bytes_per_launch": int(gu["bytes"])},
         "cpu_baseline": cpu,
-        "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "GBs": round(head["layer_GBs"], 1),
+        "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "us_eager": round(head["ms_eager"] * 1e3, 2),
+                  "timing": "HIP graph replay of the timed steps (eager time: us_eager)",
+                  "GBs": round(head["layer_GBs"], 1),
                   "frac": round(head["layer_GBs"] / HBM_PEAK_GBS, 4),
                   "active_groups": round(head["active_groups"], 2),
                   "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in head["kernels"].items()},

@@ -53,8 +53,8 @@ _SIGS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
-    "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_expert_ffn": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _I, _P, _P, _SZ, _P]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _P, _I, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_timing_enable": (_I, [_I]),
     "moe_timing_reset": (_I, []),

@@ -39,6 +39,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_init_mu;
 int g_init_state[kMaxDevices];  // 0 = not yet, 1 = ready, < 0 = status of the failure
 std::string g_init_msg[kMaxDevices];
+int g_cus[kMaxDevices];
 
 int ensure_init() {
   int dev = -1;
@@ -62,6 +63,7 @@ int ensure_init() {
     g_init_msg[dev] = g_err;
     return rc;
   }
+  g_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   std::vector<const void*> ks;
   moe::register_route_kernels(ks);
   moe::register_permute_kernels(ks);
@@ -101,6 +103,12 @@ bool sizes_ok_common(int T, int E, int K) {
 }  // namespace
 
 namespace moe {
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || g_cus[dev] <= 0) return 256;
+  return g_cus[dev];
+}
 
 int timing_begin(const char* name, hipStream_t s) {
   if (!g_timing_on.load(std::memory_order_relaxed)) return -1;
@@ -164,9 +172,9 @@ int moe_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float
 }
 
 int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t* counts,
-                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws,
-                size_t ws_bytes, void* stream) {
-  if (!ids || !counts || !offsets || !sorted_slot || !slot_pos)
+                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (!ids || !counts || !offsets || !sorted_slot || !slot_pos || !groups)
     return fail(MOE_EINVAL, "moe_permute: null pointer");
   if (!sizes_ok_common(T, E, K) || (has_shared != 0 && has_shared != 1))
     return fail(MOE_EINVAL, "moe_permute: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
@@ -176,14 +184,14 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
   int rc = ensure_init();
   if (rc != MOE_OK) return rc;
   hipError_t e = moe::launch_permute(ids, T, E, K, has_shared, counts, offsets, sorted_slot,
-                                     slot_pos, ws, (hipStream_t)stream);
+                                     slot_pos, groups, ws, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "moe_permute launch");
 }
 
 int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
-                   const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
-                   uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream) {
-  if (!W || !x || !offsets || !sorted_slot || !y_slots)
+                   const int32_t* offsets, const int32_t* sorted_slot, const int32_t* groups,
+                   int act_mode, uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !x || !offsets || !sorted_slot || !groups || !y_slots)
     return fail(MOE_EINVAL, "moe_expert_ffn: null pointer");
   if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
     return fail(MOE_EINVAL, "moe_expert_ffn: null weight pointer");
@@ -198,8 +206,8 @@ int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
     return fail(MOE_EWORKSPACE, "moe_expert_ffn: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   int rc = ensure_init();
   if (rc != MOE_OK) return rc;
-  hipError_t e = moe::launch_expert_ffn(*W, x, T, K, offsets, sorted_slot, act_mode, y_slots, ws,
-                                        (hipStream_t)stream);
+  hipError_t e = moe::launch_expert_ffn(*W, x, T, K, offsets, sorted_slot, groups, act_mode,
+                                        y_slots, ws, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn launch");
 }
 

@@ -22,18 +22,33 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int p = slot_pos[(size_t)t * K + k];
-    if (p < 0 || p >= TK) continue;
-    const float wt = w[(size_t)t * K + k];
-    const u32x4 v = *(const u32x4*)(y + (size_t)p * H + 8 * c);
+  const int ps = has_shared ? slot_pos[(size_t)TK + t] : -1;
+  // slots in batches of 16: all positions and weights of a batch are loaded,
+  // then all of its rows, then accumulated in slot order
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    int p[16];
+    float wt[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = fmaf(wt, bf16_bits_to_f32(v[j] & 0xFFFFu), acc[2 * j]);
-      acc[2 * j + 1] = fmaf(wt, bf16_bits_to_f32(v[j] >> 16), acc[2 * j + 1]);
+    for (int j = 0; j < 16; ++j) {
+      const int k = k0 + j;
+      p[j] = (k < K) ? slot_pos[(size_t)t * K + k] : -1;
+      wt[j] = (k < K) ? w[(size_t)t * K + k] : 0.f;
+    }
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = (p[j] >= 0 && p[j] < TK) ? *(const u32x4*)(y + (size_t)p[j] * H + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (p[j] >= 0 && p[j] < TK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wt[j], bf16_bits_to_f32(v[j][q] & 0xFFFFu), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wt[j], bf16_bits_to_f32(v[j][q] >> 16), acc[2 * q + 1]);
+        }
+      }
     }
   }
-  const int ps = has_shared ? slot_pos[(size_t)TK + t] : -1;
   if (ps >= 0 && ps < TK + T) {
     const u32x4 v = *(const u32x4*)(y + (size_t)ps * H + 8 * c);
 #pragma unroll

@@ -19,51 +19,10 @@
 // permutation of K that both operands share.
 #include <math.h>
 
-#include "moe_device.hpp"
+#include "moe_ffn_common.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------
-// NVFP4 -> bf16 operand conversion
-// ---------------------------------------------------------------------------
-template <int B>
-__device__ __forceinline__ uint32_t dq_pair(uint32_t word, float s) {
-  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, B);
-  v = v * s;
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// 8 e2m1 codes (one 32-bit word) times their block scale -> one bf16x8 operand.
-__device__ __forceinline__ bf16x8 dq8(uint32_t word, float s) {
-  u32x4 r = {dq_pair<0>(word, s), dq_pair<1>(word, s), dq_pair<2>(word, s), dq_pair<3>(word, s)};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8 e4m3 activation codes (two 32-bit words) -> one bf16x8 operand (exact).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
-  u32x4 r;
-  f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, false);
-  f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, 1.0f, true);
-  f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, false);
-  f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, 1.0f, true);
-  r.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
-
-// Token of a sorted slot: routed slot s -> s / K, shared slot T*K + t -> t,
-// anything else -> -1 (the row is skipped).
-__device__ __forceinline__ int slot_token(int sl, int T, int K, int has_shared) {
-  const int TK = T * K;
-  if (sl >= 0 && sl < TK) return sl / K;
-  if (has_shared && sl >= TK && sl < TK + T) return sl - TK;
-  return -1;
-}
 
 // ---------------------------------------------------------------------------
 // Per-token-row e4m3 quantisation (FP8 arm, option (a) of the issue above):
@@ -111,211 +70,6 @@ __global__ __launch_bounds__(256) void k_rowquant_e4m3(const uint16_t* __restric
       o[j] = (uint32_t)w;
     }
     out[c] = o;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Active-group lookup: the a-th group (in index order) with a non-empty row
-// range.  Every lane of the wave gets the same answer.  Returns false when
-// there are fewer than a+1 active groups.
-// ---------------------------------------------------------------------------
-__device__ bool find_active_group(const int32_t* __restrict__ offsets, int G, int a, int* e_out,
-                                  int* p0_out, int* n_out) {
-  const int lane = threadIdx.x & 63;
-  int run = 0;
-  for (int c0 = 0; c0 < G; c0 += 64) {
-    const int g = c0 + lane;
-    const int lo = (g <= G) ? offsets[g] : 0;
-    const int nx = (g + 1 <= G) ? offsets[g + 1] : lo;
-    const bool nz = g < G && nx > lo;
-    const unsigned long long m = __ballot(nz);
-    const int pc = __popcll(m);
-    if (a < run + pc) {
-      const int rank = __popcll(m & ((1ull << lane) - 1ull));
-      const unsigned long long hit = __ballot(nz && rank == a - run);
-      const int src = __ffsll((long long)hit) - 1;
-      *e_out = c0 + src;
-      *p0_out = __shfl(lo, src, 64);
-      *n_out = __shfl(nx - lo, src, 64);
-      return true;
-    }
-    run += pc;
-  }
-  return false;
-}
-
-// ---------------------------------------------------------------------------
-// Decode path (T <= 8): multi-row GEMV on 16x16x32 bf16 MFMA.
-//
-// gate_up: one block per (active group, 16 gate/up row pairs); the 4 waves
-// split K (wave w takes the 128-wide K steps w, w+4, ...), each issuing all of
-// its weight loads up front; partial sums meet in LDS and wave 0 adds them in
-// wave order and applies scale2, SiLU and the up product.
-// Lane (r = l%16, q = l/16): B column r = weight row, A row r = token row;
-// in K step s the lane owns elements 128s + 32q + [0, 32).
-// ---------------------------------------------------------------------------
-template <int SPW, bool FP8>
-__global__ __launch_bounds__(256) void k_gemv_gate_up(
-    const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
-    const float* __restrict__ scale2, const uint16_t* __restrict__ x,
-    const uint8_t* __restrict__ xq, const float* __restrict__ xs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int T, int K,
-    int H, int I, int G, int has_shared, uint16_t* __restrict__ h) {
-  __shared__ f32x4 red[4][2][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int npb = I / 16;
-  const int a = blockIdx.x / npb, pb = blockIdx.x % npb;
-  int e, p0, n;
-  if (!find_active_group(offsets, G, a, &e, &p0, &n)) return;  // same for all waves
-
-  const int r16 = lane & 15, q = lane >> 4;
-  const size_t rowb = (size_t)H / 2, srow = (size_t)H / 16;
-  const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16 + r16;
-  const uint8_t* cg = gu_codes + grow * rowb;
-  const uint8_t* cu = cg + (size_t)I * rowb;
-  const uint8_t* sg = gu_scales + grow * srow;
-  const uint8_t* su = sg + (size_t)I * srow;
-  const int nsteps = H / 128;
-
-  u32x4 wg[SPW], wu[SPW];
-  uint32_t scg[SPW], scu[SPW];
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int s = wv + 4 * i;
-    if (s < nsteps) {
-      wg[i] = *(const u32x4*)(cg + 64 * s + 16 * q);
-      wu[i] = *(const u32x4*)(cu + 64 * s + 16 * q);
-      scg[i] = *(const uint16_t*)(sg + 8 * s + 2 * q);
-      scu[i] = *(const uint16_t*)(su + 8 * s + 2 * q);
-    }
-  }
-  const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
-
-  for (int rb = 0; rb < n; rb += 16) {
-    const int r = rb + r16;
-    const int tok = (r < n) ? slot_token(sorted_slot[p0 + r], T, K, has_shared) : -1;
-    f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-      const int s = wv + 4 * i;
-      if (s < nsteps) {
-        bf16x8 av[4];
-        if (tok >= 0) {
-          if (FP8) {
-            const u32x2* src = (const u32x2*)(xq + (size_t)tok * H + 128 * s + 32 * q);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) av[w] = fp8x8_to_bf16(src[w]);
-          } else {
-            const u32x4* src = (const u32x4*)(x + (size_t)tok * H + 128 * s + 32 * q);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) av[w] = __builtin_bit_cast(bf16x8, src[w]);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) av[w] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        }
-        const float g0 = e4m3_to_f32(scg[i] & 0xFFu), g1 = e4m3_to_f32(scg[i] >> 8);
-        const float u0 = e4m3_to_f32(scu[i] & 0xFFu), u1 = e4m3_to_f32(scu[i] >> 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          dg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[w], dq8(wg[i][w], w < 2 ? g0 : g1), dg, 0, 0, 0);
-          du = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[w], dq8(wu[i][w], w < 2 ? u0 : u1), du, 0, 0, 0);
-        }
-      }
-    }
-    red[wv][0][lane] = dg;
-    red[wv][1][lane] = du;
-    __syncthreads();
-    if (wv == 0) {
-      f32x4 sgv = red[0][0][lane], suv = red[0][1][lane];
-#pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) {
-        sgv += red[w2][0][lane];
-        suv += red[w2][1][lane];
-      }
-      const int j = pb * 16 + r16;  // pair (gate row j, up row I + j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        const int rr = rb + m;
-        const int tk = __shfl(tok, m, 64);
-        if (rr < n && tk >= 0) {
-          const float rs = FP8 ? xs[tk] : 1.0f;
-          const float g = sgv[i] * s2g * rs, u = suv[i] * s2u * rs;
-          h[(size_t)(p0 + rr) * I + j] = f32_to_bf16_bits(silu_f32(g) * u);
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// down: one block per (active group, 128 output rows); wave w takes output
-// rows [32w, 32w+32) of the block as two 16-row MFMA blocks and all of K = I.
-template <int NSTEP>
-__global__ __launch_bounds__(256) void k_gemv_down(
-    const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
-    const float* __restrict__ scale2, const uint16_t* __restrict__ h,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int T, int K,
-    int H, int I, int G, int has_shared, uint16_t* __restrict__ y) {
-  constexpr int NB = 2;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int upg = H / 128;
-  const int a = blockIdx.x / upg, ub = blockIdx.x % upg;
-  int e, p0, n;
-  if (!find_active_group(offsets, G, a, &e, &p0, &n)) return;
-
-  const int r16 = lane & 15, q = lane >> 4;
-  const size_t rowb = (size_t)I / 2, srow = (size_t)I / 16;
-  const int nsteps = I / 128;  // NSTEP is this rounded up to a power of two
-  u32x4 wc[NB][NSTEP];
-  uint32_t sc[NB][NSTEP];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const size_t row = (size_t)e * H + (size_t)ub * 128 + wv * 32 + nb * 16 + r16;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      if (s < nsteps) {
-        wc[nb][s] = *(const u32x4*)(dn_codes + row * rowb + 64 * s + 16 * q);
-        sc[nb][s] = *(const uint16_t*)(dn_scales + row * srow + 8 * s + 2 * q);
-      }
-    }
-  }
-  const float s2d = scale2[3 * e + 2];
-
-  for (int rb = 0; rb < n; rb += 16) {
-    const int r = rb + r16;
-    const bool rv = r < n && slot_token(sorted_slot[p0 + r], T, K, has_shared) >= 0;
-    f32x4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      if (s >= nsteps) break;
-      bf16x8 av[4];
-      const u32x4* src = (const u32x4*)(h + (size_t)(p0 + (rv ? r : 0)) * I + 128 * s + 32 * q);
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        av[w] = __builtin_bit_cast(bf16x8, rv ? src[w] : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float c0 = e4m3_to_f32(sc[nb][s] & 0xFFu), c1 = e4m3_to_f32(sc[nb][s] >> 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[w], dq8(wc[nb][s][w], w < 2 ? c0 : c1),
-                                                            acc[nb], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = ub * 128 + wv * 32 + nb * 16 + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        const bool ok = __shfl((int)rv, m, 64) != 0;
-        if (rb + m < n && ok) y[(size_t)(p0 + rb + m) * H + col] = f32_to_bf16_bits(acc[nb][i] * s2d);
-      }
-    }
   }
 }
 
@@ -635,21 +389,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_down(
 // ---------------------------------------------------------------------------
 void register_ffn_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_rowquant_e4m3);
-  k.push_back((const void*)&k_gemv_gate_up<1, false>);
-  k.push_back((const void*)&k_gemv_gate_up<2, false>);
-  k.push_back((const void*)&k_gemv_gate_up<4, false>);
-  k.push_back((const void*)&k_gemv_gate_up<8, false>);
-  k.push_back((const void*)&k_gemv_gate_up<1, true>);
-  k.push_back((const void*)&k_gemv_gate_up<2, true>);
-  k.push_back((const void*)&k_gemv_gate_up<4, true>);
-  k.push_back((const void*)&k_gemv_gate_up<8, true>);
-  k.push_back((const void*)&k_gemv_down<1>);
-  k.push_back((const void*)&k_gemv_down<2>);
-  k.push_back((const void*)&k_gemv_down<4>);
-  k.push_back((const void*)&k_gemv_down<8>);
   k.push_back((const void*)&k_grouped_gate_up<false>);
   k.push_back((const void*)&k_grouped_gate_up<true>);
   k.push_back((const void*)&k_grouped_down);
+  register_decode_kernels(k);
 }
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -658,12 +401,14 @@ size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_m
   const size_t S = (size_t)T * K + (has_shared ? (size_t)T : 0);
   size_t b = align256(S * I * sizeof(uint16_t));
   if (act_mode == MOE_ACT_FP8_ROW) b += align256((size_t)T * H) + align256((size_t)T * sizeof(float));
+  if (T <= kDecodeMaxT && decode_supported(H, I)) b += decode_workspace_extra(T, H);
   return b;
 }
 
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
-                             const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
-                             uint16_t* y, void* ws, hipStream_t s) {
+                             const int32_t* offsets, const int32_t* sorted_slot,
+                             const int32_t* groups, int act_mode, uint16_t* y, void* ws,
+                             hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
@@ -677,40 +422,11 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
     xq = wp;
     wp += align256((size_t)T * H);
     xs = (float*)wp;
-    MOE_LAUNCH("rowquant_e4m3", s, k_rowquant_e4m3, dim3(T), dim3(256), 0, s, x, H, xq, xs);
+    wp += align256((size_t)T * sizeof(float));
   }
-  if (T <= kDecodeMaxT) {
-    // at most T*K routed groups + the shared one can be active
-    const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
-    const int nsteps = H / 128;
-    const int spw = (nsteps + 3) / 4;
-    const dim3 g1((unsigned)gmax * (I / 16)), blk(256);
-#define MOE_GEMV_GU(SPW)                                                                           \
-  do {                                                                                             \
-    if (fp8)                                                                                       \
-      MOE_LAUNCH("gemv_gate_up", s, (k_gemv_gate_up<SPW, true>), g1, blk, 0, s, W.gu_codes,        \
-                 W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, T, K, H, I, G, hs, hbuf); \
-    else                                                                                           \
-      MOE_LAUNCH("gemv_gate_up", s, (k_gemv_gate_up<SPW, false>), g1, blk, 0, s, W.gu_codes,       \
-                 W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, T, K, H, I, G, hs, hbuf); \
-  } while (0)
-    if (spw <= 1) MOE_GEMV_GU(1);
-    else if (spw <= 2) MOE_GEMV_GU(2);
-    else if (spw <= 4) MOE_GEMV_GU(4);
-    else MOE_GEMV_GU(8);
-#undef MOE_GEMV_GU
-    const int ns = I / 128;
-    const dim3 g2((unsigned)gmax * (H / 128));
-#define MOE_GEMV_DN(NS)                                                                         \
-  MOE_LAUNCH("gemv_down", s, (k_gemv_down<NS>), g2, blk, 0, s, W.dn_codes, W.dn_scales, W.scale2, \
-             hbuf, offsets, sorted_slot, T, K, H, I, G, hs, y)
-    if (ns <= 1) MOE_GEMV_DN(1);
-    else if (ns <= 2) MOE_GEMV_DN(2);
-    else if (ns <= 4) MOE_GEMV_DN(4);
-    else MOE_GEMV_DN(8);
-#undef MOE_GEMV_DN
-    return hipGetLastError();
-  }
+  if (T <= kDecodeMaxT && decode_supported(H, I))
+    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, fp8, hbuf, xq, xs, wp, y, s);
+  if (fp8) MOE_LAUNCH("rowquant_e4m3", s, k_rowquant_e4m3, dim3(T), dim3(256), 0, s, x, H, xq, xs);
   // grouped GEMM: at most S/kBM full tiles plus one partial tile per group
   const long mt_bound = (long)S / kBM + G;
   const dim3 blk(256);

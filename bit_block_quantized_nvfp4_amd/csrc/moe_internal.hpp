@@ -39,17 +39,29 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* 
 size_t permute_workspace_bytes(int T, int E, int K);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_shared,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
-                          int32_t* slot_pos, void* ws, hipStream_t s);
+                          int32_t* slot_pos, int32_t* groups, void* ws, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos, int T,
                           int K, int H, int has_shared, uint16_t* out, hipStream_t s);
 
 size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode);
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
-                             const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
-                             uint16_t* y_slots, void* ws, hipStream_t s);
+                             const int32_t* offsets, const int32_t* sorted_slot,
+                             const int32_t* groups, int act_mode, uint16_t* y_slots, void* ws,
+                             hipStream_t s);
 
 // Decode/prefill switch of moe_expert_ffn: T <= kDecodeMaxT uses the GEMV path.
 constexpr int kDecodeMaxT = 8;
+
+// Compute units of the current device (cached per device by the API layer).
+int num_cus();
+
+void register_decode_kernels(std::vector<const void*>& k);
+bool decode_supported(int H, int I);
+size_t decode_workspace_extra(int T, int H);
+hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                             const int32_t* offsets, const int32_t* sorted_slot,
+                             const int32_t* groups, bool fp8, uint16_t* hbuf, uint8_t* xq,
+                             float* xs, void* dec_ws, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

@@ -14,6 +14,8 @@
 //  * otherwise three kernels over tiles of kTileSlots slots: per-tile
 //    histograms, a per-expert scan over tiles, and the scatter (every scatter
 //    block re-derives the expert offsets from the per-expert totals).
+// Both also write the compact list of non-empty groups, which the expert FFN
+// uses to find the expert of a work unit with one load.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
 
@@ -90,6 +92,24 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, int TK, int E, in
   __syncthreads();
 }
 
+// groups[0] = number of non-empty groups, groups[1 + i] = the i-th of them in
+// index order, -1 after the last.  cnt[] holds the group counts in LDS; wave 0
+// compacts them.
+__device__ void write_groups(const int* cnt, int G, int32_t* __restrict__ groups) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int base = 0;
+  for (int c0 = 0; c0 < G; c0 += 64) {
+    const int g = c0 + lane;
+    const bool nz = g < G && cnt[g] > 0;
+    const unsigned long long m = __ballot(nz);
+    if (nz) groups[1 + base + __popcll(m & ((1ull << lane) - 1ull))] = g;
+    base += __popcll(m);
+  }
+  if (lane == 0) groups[0] = base;
+  for (int i = base + lane; i < G; i += 64) groups[1 + i] = -1;  // deterministic tail
+}
+
 // The shared group: slot T*K + t sits at position off_shared + t, both ways.
 __device__ void write_shared_group(int T, int TK, int off_shared, int32_t* __restrict__ sorted_slot,
                                    int32_t* __restrict__ slot_pos, int first, int stride) {
@@ -102,7 +122,8 @@ __device__ void write_shared_group(int T, int TK, int off_shared, int32_t* __res
 __global__ __launch_bounds__(kBlock) void k_permute_small(
     const int32_t* __restrict__ ids, int T, int E, int K, int has_shared,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
+    int32_t* __restrict__ groups) {
   __shared__ unsigned long long masks[kBlock / 64][kMaxE];
   __shared__ int run[kMaxE + 2];
   __shared__ int wsum[kBlock / 64];
@@ -117,6 +138,8 @@ __global__ __launch_bounds__(kBlock) void k_permute_small(
   }
   __syncthreads();
   for (int e = tid; e < G; e += kBlock) counts[e] = run[e];
+  write_groups(run, G, groups);
+  __syncthreads();
   const int total = block_exclusive_scan(run, G, wsum);
   for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
   if (tid == 0) offsets[G] = total;
@@ -167,7 +190,8 @@ __global__ __launch_bounds__(kBlock) void k_permute_scatter(
     const int32_t* __restrict__ ids, int T, int E, int K, int has_shared, int ntiles,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ tot,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
+    int32_t* __restrict__ groups) {
   __shared__ unsigned long long masks[kBlock / 64][kMaxE];
   __shared__ int run[kMaxE + 2];
   __shared__ int wsum[kBlock / 64];
@@ -176,8 +200,11 @@ __global__ __launch_bounds__(kBlock) void k_permute_scatter(
   for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
   for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : tot[e];
   __syncthreads();
-  if (tile == 0)
+  if (tile == 0) {
     for (int e = tid; e < G; e += kBlock) counts[e] = run[e];
+    write_groups(run, G, groups);
+  }
+  __syncthreads();
   const int total = block_exclusive_scan(run, G, wsum);
   if (tile == 0) {
     for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
@@ -209,11 +236,11 @@ size_t permute_workspace_bytes(int T, int E, int K) {
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_shared,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
-                          int32_t* slot_pos, void* ws, hipStream_t s) {
+                          int32_t* slot_pos, int32_t* groups, void* ws, hipStream_t s) {
   const int TK = T * K;
   if (TK <= kSmallSlots) {
     MOE_LAUNCH("permute_small", s, k_permute_small, dim3(1), dim3(kBlock), 0, s, ids, T, E, K,
-               has_shared, counts, offsets, sorted_slot, slot_pos);
+               has_shared, counts, offsets, sorted_slot, slot_pos, groups);
     return hipGetLastError();
   }
   const int nt = ntiles_of(TK);
@@ -222,7 +249,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_share
   MOE_LAUNCH("permute_count", s, k_permute_count, dim3(nt), dim3(kBlock), 0, s, ids, TK, E, nt, cnt);
   MOE_LAUNCH("permute_scan_tiles", s, k_permute_scan_tiles, dim3(E), dim3(kBlock), 0, s, cnt, nt, tot);
   MOE_LAUNCH("permute_scatter", s, k_permute_scatter, dim3(nt), dim3(kBlock), 0, s, ids, T, E, K,
-             has_shared, nt, cnt, tot, counts, offsets, sorted_slot, slot_pos);
+             has_shared, nt, cnt, tot, counts, offsets, sorted_slot, slot_pos, groups);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 //
 // One wave64 per token.  Lane l holds logits l, l+64, l+128, ... in registers
 // (coalesced 256-byte loads).  K rounds of a wave arg-max pick the experts in
-// rank order; the arg-max key is (logit descending, index ascending), NaN is
+// rank order (DPP inside rows of 16 lanes, readlane across rows); the arg-max
+// key is (logit descending, index ascending), NaN is
 // read as -inf, which is the tie rule of the page "handover briefs" (item A1
 // and the indexer-selection kernel spec: rank(b) counts the j with s_j > s_b or
 // s_j == s_b and j < b).  The weights are the softmax of the K selected logits
@@ -16,6 +17,43 @@
 
 namespace moe {
 
+// Order-preserving 32-bit key of a logit: larger logit -> larger key; NaN was
+// replaced by -inf; -0 is folded onto +0 so that equal logits have equal keys.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Max / min over the 64 lanes, the same value in every lane: DPP xor-1, xor-2
+// (quad permutes), half-row and row mirrors inside each row of 16 lanes, then
+// readlane of lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp<0xB1>(v));
+  v = min(v, dpp<0x4E>(v));
+  v = min(v, dpp<0x141>(v));
+  v = min(v, dpp<0x140>(v));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
+}
+
 template <int MAXV>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                      int E, int K, int32_t* __restrict__ ids,
@@ -25,48 +63,41 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
 
-  float v[MAXV];
-  uint32_t absent = 0;  // bit j: element j is selected already or does not exist
+  uint32_t key[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int e = lane + 64 * j;
     float z = -INFINITY;
     if (e < E) z = row[e];
-    else absent |= 1u << j;
-    v[j] = (z != z) ? -INFINITY : z;
+    // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
+    key[j] = (e < E) ? logit_key((z != z) ? -INFINITY : z) : 0u;
   }
 
   float zsel = -INFINITY;
   int isel = 0;
   for (int k = 0; k < K; ++k) {
-    // best untaken element of this lane: indices ascend with j, so a strict '>'
-    // keeps the lower index among equal values
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    // best remaining key of this lane; indices ascend with j, so a strict '>'
+    // keeps the lower index among equal keys
+    uint32_t bk = 0u;
+    int bj = -1;
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const bool free_j = !((absent >> j) & 1u);
-      if (free_j && (bi == INT_MAX || v[j] > bv)) {
-        bv = v[j];
-        bi = lane + 64 * j;
+    for (int j = 0; j < MAXV; ++j)
+      if (key[j] > bk) {
+        bk = key[j];
+        bj = j;
       }
-    }
-    // wave arg-max under (value desc, index asc); a total order, so the
-    // butterfly leaves the same winner in every lane
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    const uint32_t kmax = wave_max_u32(bk);
+    const uint32_t cand = (bj >= 0 && bk == kmax) ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu;
+    const int win = (int)wave_min_u32(cand);  // lowest expert index holding the max key
     if (lane == k) {
-      zsel = bv;
-      isel = bi;
+      zsel = key_logit(kmax);
+      isel = win;
     }
-    if ((bi & 63) == lane) absent |= 1u << (bi >> 6);  // bi < E because K <= E
+    if ((win & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j)
+        if (j == (win >> 6)) key[j] = 0u;  // taken: below every remaining key
+    }
   }
 
   const float z0 = __shfl(zsel, 0, 64);

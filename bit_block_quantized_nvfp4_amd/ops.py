@@ -112,17 +112,19 @@ def moe_permute(ids: torch.Tensor, E: int, has_shared: bool, ws: Optional[torch.
         out = (torch.empty(G, dtype=torch.int32, device=dev),
                torch.empty(G + 1, dtype=torch.int32, device=dev),
                torch.empty(T * K + (T if has_shared else 0), dtype=torch.int32, device=dev),
-               torch.empty(T * K + (T if has_shared else 0), dtype=torch.int32, device=dev))
-    counts, offsets, sorted_slot, slot_pos = out
+               torch.empty(T * K + (T if has_shared else 0), dtype=torch.int32, device=dev),
+               torch.empty(G + 1, dtype=torch.int32, device=dev))
+    counts, offsets, sorted_slot, slot_pos, groups = out
     nb = workspace_bytes(MOE_OP_PERMUTE, T, E, K, 0, 0, has_shared)
     ws = _workspace(nb, dev, ws)
     check(_lib.lib().moe_permute(_ptr(ids), T, E, K, int(has_shared), _ptr(counts), _ptr(offsets),
-                                 _ptr(sorted_slot), _ptr(slot_pos), _ptr(ws), nb, _stream()))
-    return counts, offsets, sorted_slot, slot_pos
+                                 _ptr(sorted_slot), _ptr(slot_pos), _ptr(groups), _ptr(ws), nb,
+                                 _stream()))
+    return counts, offsets, sorted_slot, slot_pos, groups
 
 
 def moe_expert_ffn(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tensor,
-                   sorted_slot: torch.Tensor, act_mode: int = MOE_ACT_BF16,
+                   sorted_slot: torch.Tensor, groups: torch.Tensor, act_mode: int = MOE_ACT_BF16,
                    ws: Optional[torch.Tensor] = None, y_slots: Optional[torch.Tensor] = None,
                    return_ws: bool = False):
     _need(x, torch.bfloat16, name="x")
@@ -135,12 +137,13 @@ def moe_expert_ffn(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tens
     _need(y_slots, torch.bfloat16, (S, H), "y_slots")
     _need(offsets, torch.int32, (W.E + int(W.has_shared) + 1,), "offsets")
     _need(sorted_slot, torch.int32, (S,), "sorted_slot")
+    _need(groups, torch.int32, (W.E + int(W.has_shared) + 1,), "groups")
     nb = workspace_bytes(MOE_OP_EXPERT_FFN, T, W.E, K, H, W.I, W.has_shared, act_mode)
     ws = _workspace(nb, dev, ws)
     st = W.struct()
     check(_lib.lib().moe_expert_ffn(ctypes.byref(st), _ptr(x), T, K, _ptr(offsets),
-                                    _ptr(sorted_slot), act_mode, _ptr(y_slots), _ptr(ws), nb,
-                                    _stream()))
+                                    _ptr(sorted_slot), _ptr(groups), act_mode, _ptr(y_slots),
+                                    _ptr(ws), nb, _stream()))
     return (y_slots, ws) if return_ws else y_slots
 
 
@@ -162,11 +165,11 @@ def moe_layer(W: NVFP4Weights, x: torch.Tensor, logits: torch.Tensor, K: int,
               act_mode: int = MOE_ACT_BF16) -> dict:
     """One layer call: route -> permute -> expert FFN -> combine, all on the GPU."""
     ids, w = moe_route_topk(logits, K)
-    counts, offsets, sorted_slot, slot_pos = moe_permute(ids, W.E, W.has_shared)
-    y = moe_expert_ffn(W, x, K, offsets, sorted_slot, act_mode)
+    counts, offsets, sorted_slot, slot_pos, groups = moe_permute(ids, W.E, W.has_shared)
+    y = moe_expert_ffn(W, x, K, offsets, sorted_slot, groups, act_mode)
     out = moe_combine(y, w, slot_pos, K, W.has_shared)
     return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,
-                slot_pos=slot_pos, y_slots=y, out=out)
+                slot_pos=slot_pos, groups=groups, y_slots=y, out=out)
 
 
 def timing_enable(on: bool = True) -> None:

@@ -138,6 +138,9 @@ int moe_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float
  *               offsets[E] + t (offsets[E] = T*K when every id is valid)
  *   slot_pos    [T*K + T*has_shared] int32 (out) position of slot s in
  *               sorted_slot, for the routed and the shared slots (the inverse)
+ *   groups      [E'+1] int32      (out) groups[0] = number of non-empty
+ *               groups; groups[1..groups[0]] = their indices, ascending;
+ *               the remaining entries are -1
  *   ws          device workspace of at least
  *               moe_workspace_bytes(MOE_OP_PERMUTE, T, E, K, 0, 0, has_shared, 0)
  *
@@ -146,8 +149,8 @@ int moe_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float
  * timing: positions are computed from counts, not from atomics.
  */
 int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t* counts,
-                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws,
-                size_t ws_bytes, void* stream);
+                int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups,
+                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Expert FFN of every group on the rows routed to it.  For the row of sorted
@@ -166,7 +169,8 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
  *
  *   W        host struct of device pointers, see moe_nvfp4_weights
  *   x        [T][H] bf16 bit patterns                (in)
- *   offsets  [E'+1], sorted_slot [T*K + T*has_shared] from moe_permute (in)
+ *   offsets  [E'+1], sorted_slot [T*K + T*has_shared], groups [E'+1]
+ *            from moe_permute (in)
  *   y_slots  [T*K + T*has_shared][H] bf16            (out) by sorted position
  *   ws       device workspace of at least
  *            moe_workspace_bytes(MOE_OP_EXPERT_FFN, T, E, K, H, I, has_shared, act_mode)
@@ -178,11 +182,12 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
  * Workspace contents after the call (S = T*K + T*has_shared, A(n) = n rounded
  * up to a multiple of 256): bytes [0, 2*S*I) hold h as bf16 [S][I] by sorted
  * position; with MOE_ACT_FP8_ROW the e4m3 codes [T][H] follow at byte
- * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).
+ * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).  For T <= 8 the
+ * f16 activation rows [T][H] and their fp32 epilogue factors [T] come next.
  */
 int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
-                   const int32_t* offsets, const int32_t* sorted_slot, int act_mode,
-                   uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream);
+                   const int32_t* offsets, const int32_t* sorted_slot, const int32_t* groups,
+                   int act_mode, uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Combine: out[t] = bf16( sum_{k=0..K-1} w[t][k] * y_slots[slot_pos[t*K+k]]

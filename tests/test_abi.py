@@ -40,17 +40,19 @@ def test_argument_errors_are_reported_without_a_gpu(lib):
     assert lib.moe_route_topk(one, 4, 2048, 2, one, one, None) == L.MOE_EINVAL  # E > 1024
     assert lib.moe_route_topk(one, 4, 64, 33, one, one, None) == L.MOE_EINVAL   # K > 32
     assert lib.moe_route_topk(one, 0, 8, 2, one, one, None) == L.MOE_EINVAL     # T < 1
-    assert lib.moe_permute(one, 4, 8, 2, 2, one, one, one, one, None, 0, None) == L.MOE_EINVAL
+    assert lib.moe_permute(one, 4, 8, 2, 2, one, one, one, one, one, None, 0, None) == L.MOE_EINVAL
+    assert lib.moe_permute(one, 4, 8, 2, 0, one, one, one, one, None, None, 0, None) == L.MOE_EINVAL
     # a large permute needs a workspace
-    assert lib.moe_permute(one, 4096, 512, 10, 1, one, one, one, one, None, 0, None) == L.MOE_EWORKSPACE
+    assert lib.moe_permute(one, 4096, 512, 10, 1, one, one, one, one, one, None, 0, None) == L.MOE_EWORKSPACE
     W = L.MoeNvfp4Weights(16, 16, 16, 16, 16, 8, 256, 128, 0)
     ffn = lib.moe_expert_ffn
-    assert ffn(ctypes.byref(W), one, 4, 2, one, one, 7, one, one, 1 << 20, None) == L.MOE_EUNSUPPORTED
+    assert ffn(ctypes.byref(W), one, 4, 2, one, one, one, 7, one, one, 1 << 20, None) == L.MOE_EUNSUPPORTED
     bad = L.MoeNvfp4Weights(16, 16, 16, 16, 16, 8, 200, 128, 0)   # H not a multiple of 256
-    assert ffn(ctypes.byref(bad), one, 4, 2, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
-    assert ffn(ctypes.byref(W), one, 4, 2, one, one, 0, one, one, 16, None) == L.MOE_EWORKSPACE
+    assert ffn(ctypes.byref(bad), one, 4, 2, one, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
+    assert ffn(ctypes.byref(W), one, 4, 2, one, one, one, 0, one, one, 16, None) == L.MOE_EWORKSPACE
+    assert ffn(ctypes.byref(W), one, 4, 2, one, one, None, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
     nullw = L.MoeNvfp4Weights(0, 16, 16, 16, 16, 8, 256, 128, 0)
-    assert ffn(ctypes.byref(nullw), one, 4, 2, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
+    assert ffn(ctypes.byref(nullw), one, 4, 2, one, one, one, 0, one, one, 1 << 20, None) == L.MOE_EINVAL
     assert lib.moe_combine(one, one, one, 4, 2, 12, 0, one, None) == L.MOE_EINVAL  # H % 8
     assert lib.moe_combine(one, one, None, 4, 2, 16, 0, one, None) == L.MOE_EINVAL
 

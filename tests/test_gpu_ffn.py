@@ -95,8 +95,8 @@ def test_fp8_arm(moe, cfg):
     r = _full_check(moe, wl, act_mode=1, tag=f"fp8 {cfg}")
     # the row quantisation itself is bit-exact: codes and scales sit in the workspace
     W = moe.NVFP4Weights.from_bank(wl.weights)
-    _, ws = moe.moe_expert_ffn(W, x_dev(wl.x_bf16), wl.K, r["offsets"], r["sorted_slot"], 1,
-                               return_ws=True)
+    _, ws = moe.moe_expert_ffn(W, x_dev(wl.x_bf16), wl.K, r["offsets"], r["sorted_slot"],
+                               r["groups"], 1, return_ws=True)
     torch.cuda.synchronize()
     S = wl.T * wl.K + (wl.T if wl.has_shared else 0)
     off = (S * wl.I * 2 + 255) // 256 * 256

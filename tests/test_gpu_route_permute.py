@@ -34,6 +34,10 @@ def _check_permute(moe, ids: torch.Tensor, E: int, has_shared: bool):
     want = oracle.permute(ids.cpu().numpy(), E, has_shared)
     for g, w_, name in zip(got, want, ("counts", "offsets", "sorted_slot", "slot_pos")):
         assert np.array_equal(g.cpu().numpy(), w_), name
+    active = np.nonzero(want[0])[0]
+    gr = got[4].cpu().numpy()
+    assert gr[0] == active.size and np.array_equal(gr[1:1 + active.size], active)
+    assert np.all(gr[1 + active.size:] == -1)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "long_prefill", "fp8_arm"])
@@ -100,7 +104,10 @@ def test_permute_with_duplicates_and_bad_ids(moe, T, E, K):
     slot_pos = np.full(T * K + T, -1)
     slot_pos[order] = np.arange(order.size)
     slot_pos[T * K:] = offs[E] + np.arange(T)       # the shared group follows the routed ones
-    c, o, s, p = (t.cpu().numpy() for t in got)
+    c, o, s, p, gr = (t.cpu().numpy() for t in got)
+    active = np.nonzero(np.concatenate([counts, [T]]))[0]
+    assert gr[0] == active.size and np.array_equal(gr[1:1 + active.size], active)
+    assert np.all(gr[1 + active.size:] == -1)
     assert np.array_equal(c, np.concatenate([counts, [T]]))
     assert np.array_equal(o, offs)
     n_ok = order.size
