@@ -72,6 +72,13 @@ __device__ __forceinline__ u32x2 fp8x4_to_f16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
+// One global -> LDS DMA of 16 bytes per lane: lane l's 16 bytes at g land at
+// lds + 16*l (lds is wave-uniform).  Completion is tracked like a load
+// (vmcnt); a barrier after the wait makes the data visible to the block.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));

@@ -120,99 +120,159 @@ __global__ __launch_bounds__(256) void k_dec_xprep(const uint16_t* __restrict__ 
 // contiguous quarters: lane (r16, q) owns elements [Q*q, Q*q + Q) of weight row
 // r16, Q = H/4, read as 16-byte code chunks (32 elements, one 128-element step
 // per 4 chunks); its Q/16 block scales are contiguous bytes.
+//
+// Load order (all issued before the first wait): the group lookup, then the
+// activation rows straight into LDS (global->LDS DMA, no registers), then
+// every weight word of the unit, then the epilogue's metadata.  The LDS rows
+// are unpadded with the 16-byte chunk index XOR-swizzled by (row & 15), so
+// the A-operand reads of 16 rows at one chunk hit 16 distinct bank groups.
+
+// The 2*NCH contiguous block-scale bytes of a lane (2 per 32-element chunk),
+// kept as the words they were loaded as: one load of 2, 4 or 8 bytes, or
+// 16-byte loads, so no unpacking waits on the load.
+template <int NCH>
+struct ScaleWords {
+  static constexpr int kLoads = NCH >= 8 ? NCH / 8 : 1;  // load instructions issued by load()
+  uint32_t w[NCH >= 2 ? NCH / 2 : 1];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    if constexpr (NCH == 1) {
+      w[0] = *(const uint16_t*)p;
+    } else if constexpr (NCH == 2) {
+      w[0] = *(const uint32_t*)p;
+    } else if constexpr (NCH == 4) {
+      const u32x2 v = *(const u32x2*)p;
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH / 8; ++i) {
+        const u32x4 v = *(const u32x4*)(p + 16 * i);
+        w[4 * i] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+      }
+    }
+  }
+  // scale bytes 2c (low) and 2c+1 of the run
+  __device__ __forceinline__ uint32_t pair(int c) const {
+    return NCH == 1 ? w[0] : ((c & 1) ? (w[c / 2] >> 16) : (w[c / 2] & 0xFFFFu));
+  }
+};
 
 template <int NCH>   // NCH = 16-byte code chunks per lane per row = H / 128
 struct GURegs {
   u32x4 g[NCH], u[NCH];
-  // the lane's 2*NCH scale bytes: 16-byte loads when NCH is a multiple of 8,
-  // else one 2-byte load per chunk (never past the lane's own bytes)
-  static constexpr int NS = NCH % 8 == 0 ? NCH / 8 : NCH;
-  u32x4 sg[NCH % 8 == 0 ? NCH / 8 : 1], su[NCH % 8 == 0 ? NCH / 8 : 1];
-  uint32_t sg2[NCH % 8 == 0 ? 1 : NCH], su2[NCH % 8 == 0 ? 1 : NCH];
+  ScaleWords<NCH> sg, su;
 };
 
-// scale bytes 2c, 2c+1 of the lane's contiguous run
-template <int NCH>
-__device__ __forceinline__ uint32_t scale_pair(const u32x4* sv, const uint32_t* s2, int c) {
-  if constexpr (NCH % 8 == 0) {
-    const uint32_t w = sv[c / 8][(c % 8) / 2];
-    return (c & 1) ? (w >> 16) : (w & 0xFFFFu);
-  } else {
-    return s2[c];
+// Copy rows [0, nrows) of a row-major matrix of 16-bit values (row length
+// cpr 16-byte chunks, cpr >= 16) into LDS, chunk ch of row r stored at chunk
+// position r*cpr + (ch ^ (r & 15)).  Source row r is src_row(r).  Wave wv of
+// nw moves LDS chunks [64*(wv + nw*i), +64) with one DMA instruction each.
+template <typename RowPtr>
+__device__ __forceinline__ void dma_rows_swizzled(void* lds, int nrows, int cpr, int wv, int nw,
+                                                  int lane, RowPtr src_row) {
+  const int total = nrows * cpr;
+  for (int base = 64 * wv; base < total; base += 64 * nw) {
+    const int L = base + lane;
+    if (L < total) {
+      const int r = L / cpr, ch = (L % cpr) ^ (r & 15);
+      dma16(src_row(r) + 16 * ch, (uint8_t*)lds + 16 * base);
+    }
   }
 }
 
-template <int NCH, int WPB>
-__global__ __launch_bounds__(64 * WPB) void k_dec_gate_up(
+// Byte offset in such an LDS copy of chunk ch of row r.
+__device__ __forceinline__ int swz_off(int r, int ch, int cpr) {
+  return 16 * (r * cpr + (ch ^ (r & 15)));
+}
+
+// s_waitcnt limiting only the vector-memory counter to N (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// TR = activation rows staged (T rounded up to 1, 2, 4 or 8; rows >= T repeat
+// row T-1), which makes the number of DMA instructions per wave a constant.
+template <int NCH, int WPB, int TR>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_gate_up(
     const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
     const float* __restrict__ scale2, const _Float16* __restrict__ xh,
     const float* __restrict__ unmul, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ groups, int T, int K,
     int H, int I, int has_shared, uint16_t* __restrict__ h) {
-  extern __shared__ __align__(16) _Float16 xl[];  // [T][H + 8] f16
+  extern __shared__ __align__(16) _Float16 xl[];  // [TR][H] f16, chunks swizzled
+  constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
+  constexpr int NDMA = (TR * CPR + 64 * WPB - 1) / (64 * WPB);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
-  const int ld = H + 8, Q = H / 4;
+  const int Q = H / 4;
   const int nbk = I / 16 / WPB;
   const int a = blockIdx.x / nbk, pb = (blockIdx.x % nbk) * WPB + wv;
+  // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
+  const int nact = groups[0], e = groups[1 + a];
+  asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
+  if (a >= nact) return;      // uniform per block, before any load is in flight
 
-  // activation rows into LDS: loads issued before anything that depends on the group
-  {
-    const int chunks = T * (H / 8);
-    for (int c = threadIdx.x; c < chunks; c += 64 * WPB) {
-      const int r = c / (H / 8), ch = c % (H / 8);
-      *(u32x4*)(xl + (size_t)r * ld + 8 * ch) = *(const u32x4*)(xh + (size_t)r * H + 8 * ch);
+  // (1) activation rows -> LDS
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int base = 64 * (wv + WPB * i), L = base + lane;
+    if (L < TR * CPR) {
+      const int r = L / CPR, ch = (L % CPR) ^ (r & 15);
+      dma16(xh + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
     }
   }
-  float um[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) um[i] = (4 * q + i < T) ? unmul[4 * q + i] : 0.f;
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the DMA
 
-  const bool active = a < groups[0];
-  int e = 0;
+  // (2) every weight word of the unit: 2*NCH 16-byte code loads (+ scales)
   GURegs<NCH> w;
-  if (active) {
-    e = groups[1 + a];
+  {
     const size_t rowb = (size_t)H / 2, srow = (size_t)H / 16;
     const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16 + r16;
     const uint8_t* cg = gu_codes + grow * rowb + (size_t)(Q / 2) * q;
     const uint8_t* cu = cg + (size_t)I * rowb;
     const uint8_t* sg = gu_scales + grow * srow + (size_t)(Q / 16) * q;
     const uint8_t* su = sg + (size_t)I * srow;
+    w.sg.load(sg);
+    w.su.load(su);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       w.g[c] = *(const u32x4*)(cg + 16 * c);
       w.u[c] = *(const u32x4*)(cu + 16 * c);
     }
-    if constexpr (NCH % 8 == 0) {
-#pragma unroll
-      for (int c = 0; c < NCH / 8; ++c) {
-        w.sg[c] = *(const u32x4*)(sg + 16 * c);
-        w.su[c] = *(const u32x4*)(su + 16 * c);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        w.sg2[c] = *(const uint16_t*)(sg + 2 * c);
-        w.su2[c] = *(const uint16_t*)(su + 2 * c);
-      }
-    }
   }
-  __syncthreads();  // activations in LDS
-  if (!active) return;
+  // (3) the epilogue's metadata; the slot of position `lane` is loaded for
+  // every lane (clamped into the group, n >= 1), so the loads after the DMA
+  // number at least 2*NCH + 3 on every path
   const int p0 = offsets[e], n = offsets[e + 1] - p0;
   const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
-  const int tokl = (lane < n) ? slot_token(sorted_slot[p0 + lane], T, K, has_shared) : -1;
+  float ums[8];  // unmul has T <= 8 entries in a 256-byte aligned region
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ums[t] = unmul[t];
+  const int slot_l = sorted_slot[p0 + (lane < n ? lane : n - 1)];
 
+  // (4) this wave's DMA is complete once at most the 2*NCH youngest loads are
+  // outstanding; the barrier then covers the whole block.  The weight chunks
+  // are waited for one by one as the MFMAs reach them.
+  wait_vmcnt<2 * NCH>();
+  __builtin_amdgcn_s_barrier();
+
+  // A row r16 of the MFMA = token r16; rows >= T read row T-1 (never stored)
+  const int xr = r16 < T ? r16 : T - 1;
+  const uint8_t* xrow = (const uint8_t*)xl;
   f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* xr = xl + (size_t)r16 * ld + Q * q;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const f16x2 sgv = e4m3x2_to_f16(scale_pair<NCH>(w.sg, w.sg2, c));
-    const f16x2 suv = e4m3x2_to_f16(scale_pair<NCH>(w.su, w.su2, c));
+    const f16x2 sgv = e4m3x2_to_f16(w.sg.pair(c));
+    const f16x2 suv = e4m3x2_to_f16(w.su.pair(c));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x8 av = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
-      if (r16 < T) av = *(const f16x8*)(xr + 32 * c + 8 * j);
+      const f16x8 av = *(const f16x8*)(xrow + swz_off(xr, (Q / 8) * q + 4 * c + j, CPR));
       dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w.g[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
       du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w.u[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
     }
@@ -221,10 +281,12 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_gate_up(
   uint16_t hv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float g = dg[i] * um[i] * s2g, u = du[i] * um[i] * s2u;
+    const float um = q == 0 ? ums[i] : (q == 1 ? ums[4 + i] : 0.f);  // tokens >= 8 are never stored
+    const float g = dg[i] * um * s2g, u = du[i] * um * s2u;
     hv[i] = f32_to_bf16_bits(silu_f32(g) * u);
   }
   // position p of the group holds token tok(p); lane (tok/4, col) has its row
+  const int tokl = slot_token(slot_l, T, K, has_shared);
   const int j = pb * 16 + r16;
   for (int p = 0; p < n; ++p) {
     const int tok = p < 64 ? __shfl(tokl, p, 64) : slot_token(sorted_slot[p0 + p], T, K, has_shared);
@@ -238,62 +300,57 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_gate_up(
 // --------------------------------- down -----------------------------------
 // One wave = one unit (group, 64 output rows as 4 MFMA blocks of 16, all of
 // K = I); a block holds WPB consecutive units of one group and the group's h
-// rows (up to 16 per pass) in LDS.  Lane (r16, q) owns K elements
-// [Q*q, Q*q + Q), Q = I/4, as 16-byte code chunks; its Q/16 scale bytes are
-// contiguous.
+// rows (up to 16 per pass) in LDS, chunk-swizzled like the activations above.
+// Lane (r16, q) owns K elements [Q*q, Q*q + Q), Q = I/4, as 16-byte code
+// chunks; its Q/16 scale bytes are contiguous.  Every position of a group's
+// range is a valid slot (the permutation only places valid ones), so the rows
+// are read without a slot lookup; rows of a pass past the group's end repeat
+// its last row and are not stored.
 
 template <int NCH>   // NCH = I / 128
 struct DNRegs {
   u32x4 c[4][NCH];
-  uint32_t s[4][NCH];  // 2 scale bytes per chunk, in the low half
+  ScaleWords<NCH> s[4];
 };
 
 template <int NCH, int WPB>
 __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
     const float* __restrict__ scale2, const uint16_t* __restrict__ h,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot,
-    const int32_t* __restrict__ groups, int T, int K, int H, int I, int has_shared,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ groups, int H, int I,
     uint16_t* __restrict__ y) {
-  extern __shared__ __align__(16) uint16_t hl[];  // [16][I + 8]: h rows of one pass
-  __shared__ int rvl[16];
+  extern __shared__ __align__(16) uint16_t hl[];  // [16][I] bf16, chunks swizzled
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
-  const int Q = I / 4, ldh = I + 8;
+  const int Q = I / 4, cpr = I / 8;
   const int nbk = H / 64 / WPB;
   const int a = blockIdx.x / nbk, rb = (blockIdx.x % nbk) * WPB + wv;
-  if (a >= groups[0]) return;  // uniform per block
-  const int e = groups[1 + a];
-  const size_t rowb = (size_t)I / 2, srow = (size_t)I / 16;
+  const int nact = groups[0], e = groups[1 + a];
+  asm volatile("" ::"s"(e));  // both lookups in one trip
+  if (a >= nact) return;      // uniform per block
   DNRegs<NCH> w;
+  {
+    const size_t rowb = (size_t)I / 2, srow = (size_t)I / 16;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const size_t row = (size_t)e * H + (size_t)rb * 64 + nb * 16 + r16;
-    const uint8_t* cr = dn_codes + row * rowb + (size_t)(Q / 2) * q;
-    const uint8_t* sr = dn_scales + row * srow + (size_t)(Q / 16) * q;
+    for (int nb = 0; nb < 4; ++nb) {
+      const size_t row = (size_t)e * H + (size_t)rb * 64 + nb * 16 + r16;
+      const uint8_t* cr = dn_codes + row * rowb + (size_t)(Q / 2) * q;
+      const uint8_t* sr = dn_scales + row * srow + (size_t)(Q / 16) * q;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      w.c[nb][c] = *(const u32x4*)(cr + 16 * c);
-      w.s[nb][c] = *(const uint16_t*)(sr + 2 * c);
+      for (int c = 0; c < NCH; ++c) w.c[nb][c] = *(const u32x4*)(cr + 16 * c);
+      w.s[nb].load(sr);
     }
   }
+  asm volatile("" ::: "memory");  // the group's row range is looked up after the weights are requested
   const int p0 = offsets[e], n = offsets[e + 1] - p0;
   const float s2d = scale2[3 * e + 2];
-  for (int r0 = 0; r0 < n; r0 += 16) {  // one pass unless ids repeat (> 16 rows)
-    if (r0 > 0) __syncthreads();          // previous pass done reading hl
-    for (int c = threadIdx.x; c < 16 * (I / 8); c += 64 * WPB) {
-      const int r = c / (I / 8), ch = c % (I / 8);
-      const int m = r0 + r;
-      const bool rv = m < n && slot_token(sorted_slot[p0 + m], T, K, has_shared) >= 0;
-      *(u32x4*)(&hl[r * ldh + 8 * ch]) = rv ? *(const u32x4*)(h + (size_t)(p0 + m) * I + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-      if (ch == 0) rvl[r] = rv ? 1 : 0;
-    }
+  const uint8_t* hrow = (const uint8_t*)hl;
+  // rows [r0, r0 + 16) of the group: stage, multiply, store
+  auto pass = [&](int r0) {
+    const int last = (n - r0 < 16 ? n - r0 : 16) - 1;
+    dma_rows_swizzled(hl, 16, cpr, wv, WPB, lane, [&](int r) {
+      return (const uint8_t*)(h + (size_t)(p0 + r0 + (r < last ? r : last)) * I);
+    });
     __syncthreads();
-    // the weight words count as redefined on every pass, so the dequantised
-    // operands (4x the registers of the codes) are not hoisted out of the loop
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w.c[nb][c]));
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -302,12 +359,13 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
       float sc[4][2];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        sc[nb][0] = e4m3_to_f32(w.s[nb][c] & 0xFFu);
-        sc[nb][1] = e4m3_to_f32((w.s[nb][c] >> 8) & 0xFFu);
+        const uint32_t sp = w.s[nb].pair(c);
+        sc[nb][0] = e4m3_to_f32(sp & 0xFFu);
+        sc[nb][1] = e4m3_to_f32((sp >> 8) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(&hl[r16 * ldh + Q * q + 32 * c + 8 * j]));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(hrow + swz_off(r16, (Q / 8) * q + 4 * c + j, cpr)));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dq8(w.c[nb][c][j], sc[nb][j >> 1]), acc[nb], 0, 0, 0);
@@ -322,9 +380,26 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int mm = 4 * q + i;
-        if (r0 + mm < n && rvl[mm]) y[(size_t)(p0 + r0 + mm) * H + col] = f32_to_bf16_bits(acc[nb][i] * s2d);
+        if (r0 + mm < n) y[(size_t)(p0 + r0 + mm) * H + col] = f32_to_bf16_bits(acc[nb][i] * s2d);
       }
     }
+  };
+  // The first pass is straight-line code: a loop whose body reads the weight
+  // registers would first wait for every outstanding load, and the h rows must
+  // be requested before that wait.
+  pass(0);
+  for (int r0 = 16; r0 < n; r0 += 16) {  // only when ids repeat (> 16 rows)
+    __syncthreads();  // previous pass done reading hl
+    // the weight words count as redefined on every pass, so the dequantised
+    // operands (4x the registers of the codes) are not hoisted out of the loop
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w.c[nb][c]));
+#pragma unroll
+      for (int c = 0; c < (NCH >= 2 ? NCH / 2 : 1); ++c) asm volatile("" : "+v"(w.s[nb].w[c]));
+    }
+    pass(r0);
   }
 }
 
@@ -333,14 +408,20 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 void register_decode_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_dec_xprep<false>);
   k.push_back((const void*)&k_dec_xprep<true>);
-  k.push_back((const void*)&k_dec_gate_up<2, 1>);
-  k.push_back((const void*)&k_dec_gate_up<2, 4>);
-  k.push_back((const void*)&k_dec_gate_up<4, 1>);
-  k.push_back((const void*)&k_dec_gate_up<4, 4>);
-  k.push_back((const void*)&k_dec_gate_up<8, 1>);
-  k.push_back((const void*)&k_dec_gate_up<8, 4>);
-  k.push_back((const void*)&k_dec_gate_up<16, 1>);
-  k.push_back((const void*)&k_dec_gate_up<16, 4>);
+#define MOE_REG_GU(NCH)                                  \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 1>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 2>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 4>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 8>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 1>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 2>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 4>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 8>);
+  MOE_REG_GU(2)
+  MOE_REG_GU(4)
+  MOE_REG_GU(8)
+  MOE_REG_GU(16)
+#undef MOE_REG_GU
   k.push_back((const void*)&k_dec_down<1, 1>);
   k.push_back((const void*)&k_dec_down<1, 4>);
   k.push_back((const void*)&k_dec_down<2, 1>);
@@ -385,35 +466,44 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const long cus = num_cus();
   const int wpb_g = gu_units >= 8 * cus ? 4 : 1;
   const int wpb_d = dn_units >= 8 * cus ? 4 : 1;
-  const size_t lds_gu = (size_t)T * (H + 8) * sizeof(_Float16);
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
+  const size_t lds_gu = (size_t)tr * H * sizeof(_Float16);
   const dim3 g1((unsigned)(gu_units / wpb_g)), b1(64 * wpb_g);
   const int nch = H / 128;
-#define MOE_DEC_GU(NCH)                                                                             \
-  do {                                                                                              \
-    if (wpb_g == 4)                                                                                 \
-      MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, 4>), g1, b1, lds_gu, s, W.gu_codes,          \
-                 W.gu_scales, W.scale2, xh, unmul, offsets, sorted_slot, groups, T, K, H, I, hs, hbuf); \
-    else                                                                                            \
-      MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, 1>), g1, b1, lds_gu, s, W.gu_codes,          \
-                 W.gu_scales, W.scale2, xh, unmul, offsets, sorted_slot, groups, T, K, H, I, hs, hbuf); \
+#define MOE_DEC_GU1(NCH, WPB, TR)                                                                    \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR>), g1, b1, lds_gu, s, W.gu_codes,        \
+             W.gu_scales, W.scale2, xh, unmul, offsets, sorted_slot, groups, T, K, H, I, hs, hbuf)
+#define MOE_DEC_GU2(NCH, WPB)                   \
+  do {                                          \
+    if (tr == 1) MOE_DEC_GU1(NCH, WPB, 1);      \
+    else if (tr == 2) MOE_DEC_GU1(NCH, WPB, 2); \
+    else if (tr == 4) MOE_DEC_GU1(NCH, WPB, 4); \
+    else MOE_DEC_GU1(NCH, WPB, 8);              \
+  } while (0)
+#define MOE_DEC_GU(NCH)                       \
+  do {                                        \
+    if (wpb_g == 4) MOE_DEC_GU2(NCH, 4);      \
+    else MOE_DEC_GU2(NCH, 1);                 \
   } while (0)
   if (nch == 2) MOE_DEC_GU(2);
   else if (nch == 4) MOE_DEC_GU(4);
   else if (nch == 8) MOE_DEC_GU(8);
   else if (nch == 16) MOE_DEC_GU(16);
   else return hipErrorInvalidValue;
+#undef MOE_DEC_GU2
+#undef MOE_DEC_GU1
 #undef MOE_DEC_GU
   const dim3 g2((unsigned)(dn_units / wpb_d)), b2(64 * wpb_d);
-  const size_t lds_dn = (size_t)16 * (I + 8) * sizeof(uint16_t);
+  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t);
   const int ncd = I / 128;
 #define MOE_DEC_DN(NCH)                                                                            \
   do {                                                                                             \
     if (wpb_d == 4)                                                                                \
       MOE_LAUNCH("dec_down", s, (k_dec_down<NCH, 4>), g2, b2, lds_dn, s, W.dn_codes, W.dn_scales,       \
-                 W.scale2, hbuf, offsets, sorted_slot, groups, T, K, H, I, hs, y);                 \
+                 W.scale2, hbuf, offsets, groups, H, I, y);                 \
     else                                                                                           \
       MOE_LAUNCH("dec_down", s, (k_dec_down<NCH, 1>), g2, b2, lds_dn, s, W.dn_codes, W.dn_scales,       \
-                 W.scale2, hbuf, offsets, sorted_slot, groups, T, K, H, I, hs, y);                 \
+                 W.scale2, hbuf, offsets, groups, H, I, y);                 \
   } while (0)
   if (ncd == 1) MOE_DEC_DN(1);
   else if (ncd == 2) MOE_DEC_DN(2);
