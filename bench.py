@@ -155,6 +155,44 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{dt:.1f} s, numpy BLAS threads = host cores"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def counter_pass(moe, torch, banks, base, steps):
+    """Eager layer calls for hardware-counter runs (one kernel per dispatch).
+
+    Prints one line per phase; the counters of each kernel are read from the
+    profiler's per-dispatch output.  The copy moves COPY_BYTES (read) into
+    COPY_BYTES (written) with torch's elementwise copy kernel, so its
+    FETCH_SIZE / WRITE_SIZE give the factor between the counters and bytes.
+    """
+    from workloads import workload_for
+
+    wl = workload_for("decode", T=8, with_weights=False)
+    wl.weights = base.weights
+    lsets = [workload_for("decode", T=8, seed=s, with_weights=False).logits for s in range(NLOGITS)]
+    r = LayerRunner(moe, torch, banks, wl, lsets)
+    for i in range(steps):
+        r.run(i)
+    torch.cuda.synchronize()
+    act = r.active_groups()
+    print(f"# counter pass: decode T=8, {steps} layer calls, active groups per logits set {act}",
+          file=sys.stderr, flush=True)
+    wl = workload_for("prefill", with_weights=False)
+    wl.weights = base.weights
+    r = LayerRunner(moe, torch, banks, wl, [wl.logits])
+    for i in range(3):
+        r.run(i)
+    torch.cuda.synchronize()
+    print("# counter pass: prefill T=4096, 3 layer calls", file=sys.stderr, flush=True)
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"# counter pass: 3 copies of {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +201,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the T=1,2,4 and prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="eager launches only, for rocprofv3 --pmc: the T=8 decode layer, the T=4096 "
+                         "prefill layer and a plain copy of COPY_BYTES (the counters' scale reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -194,6 +235,10 @@ def main():
     H, I = base.H, base.I
     print(f"# {NBANKS} weight banks of {base.weights.bytes_per_expert * (base.E + 1) / 1e6:.1f} MB",
           file=sys.stderr, flush=True)
+
+    if args.counter_pass:
+        counter_pass(moe, torch, banks, base, args.steps)
+        return
 
     def decode_line(T, steps, warmup):
         wl = workload_for("decode", T=T, with_weights=False)

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_dec_xprep(const uint16_t* __restrict__ 
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float mul;
   if (FP8) {
-    // the row quantisation of the FP8 arm (same rule as k_rowquant_e4m3)
+    // the row quantisation of the FP8 arm: s = absmax/448, codes e4m3(x * 448/absmax)
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
     mul = amax > 0.f ? 448.0f / amax : 1.0f;
     if (tid == 0) {
@@ -441,6 +441,17 @@ bool decode_supported(int H, int I) {
          (ncd == 1 || ncd == 2 || ncd == 4 || ncd == 8);
 }
 
+// One block per token row (H <= 4096): f16 rows and epilogue factors, and
+// for the FP8 arm the e4m3 codes and row scales.
+hipError_t launch_xprep(const uint16_t* x, int T, int H, bool fp8, _Float16* xh, float* unmul,
+                        uint8_t* xq, float* xs, hipStream_t s) {
+  if (fp8)
+    MOE_LAUNCH("xprep", s, (k_dec_xprep<true>), dim3(T), dim3(256), 0, s, x, H, xh, unmul, xq, xs);
+  else
+    MOE_LAUNCH("xprep", s, (k_dec_xprep<false>), dim3(T), dim3(256), 0, s, x, H, xh, unmul, xq, xs);
+  return hipGetLastError();
+}
+
 // f16 activation rows [T][H] and their epilogue factors [T].
 size_t decode_workspace_extra(int T, int H) {
   return align256((size_t)T * H * sizeof(_Float16)) + align256((size_t)T * sizeof(float));
@@ -455,11 +466,8 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
   _Float16* xh = (_Float16*)dec_ws;
   float* unmul = (float*)((uint8_t*)dec_ws + align256((size_t)T * H * sizeof(_Float16)));
-  const dim3 blk(256);
-  if (fp8)
-    MOE_LAUNCH("dec_xprep", s, (k_dec_xprep<true>), dim3(T), blk, 0, s, x, H, xh, unmul, xq, xs);
-  else
-    MOE_LAUNCH("dec_xprep", s, (k_dec_xprep<false>), dim3(T), blk, 0, s, x, H, xh, unmul, xq, xs);
+  hipError_t pe = launch_xprep(x, T, H, fp8, xh, unmul, xq, xs, s);
+  if (pe != hipSuccess) return pe;
   // Waves (units) per block: 4 when there are enough units to fill the
   // chip, else 1 so that small T still spreads over many CUs.
   const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
@@ -468,6 +476,7 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const int wpb_d = dn_units >= 8 * cus ? 4 : 1;
   const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
   const size_t lds_gu = (size_t)tr * H * sizeof(_Float16);
+  const dim3 blk(256);
   const dim3 g1((unsigned)(gu_units / wpb_g)), b1(64 * wpb_g);
   const int nch = H / 128;
 #define MOE_DEC_GU1(NCH, WPB, TR)                                                                    \

@@ -1,0 +1,365 @@
+// Prefill expert FFN (T > 8 tokens): grouped GEMM on 32x32x16 MFMA, one
+// kernel template for both projections.
+//
+//   gate_up (GU): A = f16 activation rows gathered by token (x with a per-row
+//                 power-of-two shift, or the exact f16 value of the FP8 arm's
+//                 e4m3 codes), B = NVFP4 gate/up rows dequantised to f16 (one
+//                 instruction per element), f32 accumulate; epilogue
+//                 h = bf16(silu(g * s2g * f_t) * (u * s2u * f_t)), f_t the
+//                 row's epilogue factor.
+//   down (DN):    A = bf16 h rows (contiguous sorted positions), B = NVFP4 down
+//                 rows dequantised to bf16, epilogue y = bf16(acc * s2d).
+//
+// Work item = (group, 128-row tile of its sorted rows, N tile).  A block of NW
+// waves owns 64*NW weight rows of the N tile: wave w holds two 32-row MFMA
+// blocks (GU: 32 gate rows and the 32 up rows of the same pairs; DN: rows
+// 32w and 32*NW + 32w of the tile) against all 128 tile rows (four 32-row
+// blocks, the ones past the group's end skipped).  Every weight byte is
+// dequantised exactly once per block; the A tile is shared by all waves.
+//
+// K runs in steps of 128.  Each step's A tile (128 rows x 256 B), weight
+// codes (64*NW rows x 64 B) and block scales (64*NW rows x 8 B) are loaded by
+// all threads with row-contiguous 16-byte accesses (every 64 B of a weight row
+// by 4 adjacent lanes) into registers while the previous step computes, then
+// written to the other half of a double-buffered LDS stage; one barrier per
+// step.  LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand
+// reads of 16 consecutive rows at one chunk hit distinct banks.
+//
+// Lane (n = l%32, q = l/32) of sub-step (c, wd), c in {0,1}, wd in 0..3: MFMA
+// k index 8q + i is element 64c + 32q + 8wd + i of the step on both operands
+// (weight bytes 32c + 16q + 4wd + i/2 of the row's 64-byte step slice, block
+// 4c + 2q + wd/2), so the sums run over all of K.
+#include "moe_ffn_common.hpp"
+#include "moe_internal.hpp"
+
+namespace moe {
+
+constexpr int kPM = 128;   // rows per tile
+constexpr int kPK = 128;   // K per step
+constexpr int kPMaxG = 1025;
+
+__device__ __forceinline__ int pf_xcd_remap(int b, int nb) {
+  // blocks b = x, x+8, x+16, ... run on XCD x: give each XCD a contiguous run
+  // of items, so the tiles that share a weight tile (or an A tile) share its L2
+  const int q = nb / 8, r = nb % 8, xcd = b % 8, i = b / 8;
+  return (xcd < r) ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+}
+
+struct PfTile {
+  int g, p0, rows, nt;
+};
+
+// Item lookup from offsets: items are enumerated group by group, N tile by N
+// tile, row tile by row tile.  All threads must call it; false = no item.
+template <int NTHR>
+__device__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT, int* base,
+                             int* wsum, PfTile* ti) {
+  constexpr int NWV = NTHR / 64;
+  const int tid = threadIdx.x;
+  for (int g = tid; g < G; g += NTHR) {
+    const int cnt = offsets[g + 1] - offsets[g];
+    base[g] = cnt > 0 ? (cnt + kPM - 1) / kPM : 0;
+  }
+  __syncthreads();
+  const int per = (G + NTHR - 1) / NTHR;
+  const int lo = min(tid * per, G), hi = min(lo + per, G);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += base[i];
+  const int lane = tid & 63, wv = tid >> 6;
+  const int incl = wave_incl_scan(local, lane);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) {
+    before += (i < wv) ? wsum[i] : 0;
+    total += wsum[i];
+  }
+  int run = before + incl - local;
+  for (int i = lo; i < hi; ++i) {
+    const int v = base[i];
+    base[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  const int L = pf_xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= total * NT) return false;
+  // last g with base[g] * NT <= L; empty groups share the base of the next
+  // non-empty one, so the search lands on the group that owns L
+  int lo_g = 0, hi_g = G - 1;
+  while (lo_g < hi_g) {
+    const int mid = (lo_g + hi_g + 1) >> 1;
+    if (base[mid] * NT <= L) lo_g = mid;
+    else hi_g = mid - 1;
+  }
+  const int g = lo_g;
+  const int mt_g = ((offsets[g + 1] - offsets[g]) + kPM - 1) / kPM;
+  const int li = L - base[g] * NT;
+  ti->g = g;
+  ti->nt = li / mt_g;
+  ti->p0 = offsets[g] + (li % mt_g) * kPM;
+  ti->rows = min(kPM, offsets[g + 1] - ti->p0);
+  return true;
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Shared memory of one block (one work item at a time).
+template <int NW>
+struct PfSmem {
+  static constexpr int WR = 64 * NW;
+  uint8_t As[2][kPM * 256];  // A tile of a K step, 16-byte chunks swizzled by (row & 15)
+  uint8_t Ws[2][WR * 64];    // weight codes of a K step, chunks swizzled by ((row >> 2) & 3)
+  uint8_t Ss[2][WR * 8];     // block scales of a K step
+  int base[kPMaxG];
+  int wsum[NW];
+  int row_src[kPM];          // GU: token of the row; DN: sorted position (valid even for padding)
+  float row_fac[kPM];        // GU: epilogue factor of the row's token
+  int row_ok[kPM];
+};
+
+// The K loop and epilogue of one work item with NMB valid 32-row blocks
+// (compile-time, so the MFMA schedule has no branches).
+template <int NW, bool GU, int NMB>
+__device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
+                                        const uint8_t* __restrict__ codes,
+                                        const uint8_t* __restrict__ scales,
+                                        const float* __restrict__ scale2,
+                                        const uint16_t* __restrict__ asrc, int H, int I,
+                                        uint16_t* __restrict__ out) {
+  constexpr int NTHR = 64 * NW;
+  constexpr int WR = 64 * NW;           // weight rows of a tile
+  constexpr int ACH = kPM * 16 / NTHR;  // A 16-byte chunks per thread per step
+  constexpr int WCH = WR * 4 / NTHR;    // weight 16-byte chunks per thread per step
+  static_assert(WCH == 4, "4 weight chunks per thread");
+  const int KD = GU ? H : I;  // reduction length
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = ti.g;
+
+  // ---- per-thread load addresses (fixed across K steps) ----
+  const size_t rowb = (size_t)KD / 2, srow = (size_t)KD / 16;
+  auto wrow = [&](int rho) -> size_t {  // global weight row of tile row rho
+    if (GU) {
+      const int half = 32 * NW;
+      return (size_t)e * 2 * I + (rho < half ? (size_t)ti.nt * half + rho
+                                            : (size_t)I + (size_t)ti.nt * half + (rho - half));
+    }
+    return (size_t)e * H + (size_t)ti.nt * WR + rho;
+  };
+  const uint8_t* wsrc[WCH];
+  int wdst[WCH];
+#pragma unroll
+  for (int j = 0; j < WCH; ++j) {
+    const int L = tid + NTHR * j, rho = L >> 2, cp = L & 3;
+    wsrc[j] = codes + wrow(rho) * rowb + 16 * cp;
+    wdst[j] = rho * 64 + 16 * (cp ^ ((rho >> 2) & 3));
+  }
+  const uint8_t* ssrc = scales + wrow(tid) * srow;  // WR == NTHR rows: one per thread
+  const uint8_t* asrc_p[ACH];
+  int adst[ACH];
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) {
+    const int L = tid + NTHR * j, r = L >> 4, ch = L & 15;
+    asrc_p[j] = (const uint8_t*)(asrc + (size_t)sm.row_src[r] * KD) + 16 * ch;
+    adst[j] = r * 256 + 16 * (ch ^ (r & 15));
+  }
+
+  u32x4 ra[ACH], rw[WCH];
+  u32x2 rs;
+  auto load_step = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) ra[j] = *(const u32x4*)(asrc_p[j] + 256 * s);
+#pragma unroll
+    for (int j = 0; j < WCH; ++j) rw[j] = *(const u32x4*)(wsrc[j] + 64 * s);
+    rs = *(const u32x2*)(ssrc + 8 * s);
+  };
+  auto store_step = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) *(u32x4*)(&sm.As[st][adst[j]]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < WCH; ++j) *(u32x4*)(&sm.Ws[st][wdst[j]]) = rw[j];
+    *(u32x2*)(&sm.Ss[st][tid * 8]) = rs;
+  };
+
+  const int n32 = lane & 31, q = lane >> 5;
+  int rho_b[2];
+  rho_b[0] = 32 * wv + n32;
+  rho_b[1] = 32 * NW + 32 * wv + n32;
+
+  f32x16 acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+
+  const int nsteps = KD / kPK;
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int st = s & 1;
+    if (s + 1 < nsteps) load_step(s + 1);
+    const uint8_t* A = sm.As[st];
+    const uint8_t* Wt = sm.Ws[st];
+    const uint8_t* St = sm.Ss[st];
+    u32x2 sw[2];
+    u32x4 wc[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int rho = rho_b[nb];
+      sw[nb] = *(const u32x2*)(St + rho * 8);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int cp = 2 * c + q;
+        wc[c][nb] = *(const u32x4*)(Wt + rho * 64 + 16 * (cp ^ ((rho >> 2) & 3)));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // this lane's two block scales of chunk c: bytes 4c + 2q, 4c + 2q + 1
+      uint32_t sp[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) sp[nb] = q ? (sw[nb][c] >> 16) : sw[nb][c];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int ach = 8 * c + 4 * q + wd;
+        u32x4 av[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int r = 32 * mb + n32;
+          av[mb] = *(const u32x4*)(A + r * 256 + 16 * (ach ^ (r & 15)));
+        }
+        u32x4 b[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (GU) {
+            const f16x2 sv = e4m3x2_to_f16(sp[nb]);
+            b[nb] = __builtin_bit_cast(u32x4, dqh8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+          } else {
+            const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[nb], 1.0f, false);
+            b[nb] = __builtin_bit_cast(u32x4, dq8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (GU)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  as_f16x8(av[mb]), as_f16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+            else
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(av[mb]), as_bf16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (s + 1 < nsteps) store_step(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  if (GU) {
+    const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
+    const int col = ti.nt * 32 * NW + 32 * wv + n32;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * mb + 8 * (i >> 2) + 4 * q + (i & 3);
+        if (r < ti.rows && sm.row_ok[r]) {
+          const float f = sm.row_fac[r];
+          const float g = acc[mb][0][i] * s2g * f, u = acc[mb][1][i] * s2u * f;
+          out[(size_t)(ti.p0 + r) * I + col] = f32_to_bf16_bits(silu_f32(g) * u);
+        }
+      }
+    }
+  } else {
+    const float s2d = scale2[3 * e + 2];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = ti.nt * WR + 32 * NW * nb + 32 * wv + n32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 32 * mb + 8 * (i >> 2) + 4 * q + (i & 3);
+          if (r < ti.rows && sm.row_ok[r])
+            out[(size_t)(ti.p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][i] * s2d);
+        }
+      }
+    }
+  }
+}
+
+template <int NW, bool GU>
+__global__ __launch_bounds__(64 * NW, 1) void k_prefill_gemm(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ scale2, const uint16_t* __restrict__ asrc,
+    const float* __restrict__ rowfac, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slot, int T, int K, int H, int I, int G, int has_shared,
+    uint16_t* __restrict__ out) {
+  constexpr int NTHR = 64 * NW;
+  __shared__ __align__(16) PfSmem<NW> sm;
+  const int NT = GU ? I / (32 * NW) : H / (64 * NW);  // N tiles per group
+  PfTile ti;
+  if (!pf_find_tile<NTHR>(offsets, G, NT, sm.base, sm.wsum, &ti)) return;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < kPM; r += NTHR) {
+    int src = -1;
+    if (r < ti.rows) {
+      const int tk = slot_token(sorted_slot[ti.p0 + r], T, K, has_shared);
+      src = tk < 0 ? -1 : (GU ? tk : ti.p0 + r);
+    }
+    sm.row_ok[r] = src >= 0;
+    sm.row_src[r] = src >= 0 ? src : (GU ? 0 : ti.p0);  // a valid row to read for padding rows
+    if (GU) sm.row_fac[r] = src >= 0 ? rowfac[src] : 0.f;
+  }
+  __syncthreads();
+  switch ((ti.rows + 31) / 32) {  // uniform per block
+    case 1: pf_item<NW, GU, 1>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
+    case 2: pf_item<NW, GU, 2>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
+    case 3: pf_item<NW, GU, 3>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
+    default: pf_item<NW, GU, 4>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
+  }
+}
+
+void register_prefill_kernels(std::vector<const void*>& k) {
+  k.push_back((const void*)&k_prefill_gemm<8, true>);
+  k.push_back((const void*)&k_prefill_gemm<4, true>);
+  k.push_back((const void*)&k_prefill_gemm<8, false>);
+  k.push_back((const void*)&k_prefill_gemm<4, false>);
+}
+
+hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
+                              const int32_t* sorted_slot, const _Float16* xh, const float* rowfac,
+                              uint16_t* hbuf, uint16_t* y, hipStream_t s) {
+  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
+  const int G = W.E + hs;
+  const long S = (long)T * K + (hs ? T : 0);
+  // at most S/kPM full row tiles plus one partial tile per group
+  const long mt_bound = S / kPM + G;
+  const uint16_t* xa = (const uint16_t*)xh;
+  if (I % 256 == 0) {
+    const dim3 g1((unsigned)(mt_bound * (I / 256)));
+    MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<8, true>), g1, dim3(512), 0, s, W.gu_codes,
+               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
+  } else {
+    const dim3 g1((unsigned)(mt_bound * (I / 128)));
+    MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<4, true>), g1, dim3(256), 0, s, W.gu_codes,
+               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
+  }
+  if (H % 512 == 0) {
+    const dim3 g2((unsigned)(mt_bound * (H / 512)));
+    MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<8, false>), g2, dim3(512), 0, s, W.dn_codes,
+               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
+  } else {
+    const dim3 g2((unsigned)(mt_bound * (H / 256)));
+    MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<4, false>), g2, dim3(256), 0, s, W.dn_codes,
+               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -57,6 +57,15 @@ constexpr int kDecodeMaxT = 8;
 int num_cus();
 
 void register_decode_kernels(std::vector<const void*>& k);
+void register_prefill_kernels(std::vector<const void*>& k);
+// Per-row activation prep shared by both regimes: f16 rows xh [T][H] (bf16
+// arm: x * 2^sh with unmul = 2^-sh; FP8 arm: the exact f16 value of each e4m3
+// code with unmul = the row scale, codes and scales also written to xq, xs).
+hipError_t launch_xprep(const uint16_t* x, int T, int H, bool fp8, _Float16* xh, float* unmul,
+                        uint8_t* xq, float* xs, hipStream_t s);
+hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
+                              const int32_t* sorted_slot, const _Float16* xh, const float* rowfac,
+                              uint16_t* hbuf, uint16_t* y, hipStream_t s);
 bool decode_supported(int H, int I);
 size_t decode_workspace_extra(int T, int H);
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
