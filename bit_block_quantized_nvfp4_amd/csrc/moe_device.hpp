@@ -1,5 +1,5 @@
 // Device-side helpers shared by the gfx950 kernels of the NVFP4 MoE layer:
-// vector types, bf16 <-> f32, e4m3 decode, wave-level reductions and scans.
+// vector types, bf16 <-> f32, wave-level reductions and scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,15 +31,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // Two f32 -> packed bf16 pair (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-}
-
-// OCP e4m3 ("fn") byte -> f32: bias 7, exponent field 0 is subnormal
-// (m * 2^-9), S.1111.111 is NaN, no infinities.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  if (e == 15u && m == 7u) mag = __builtin_nanf("");
-  return (b & 0x80u) ? -mag : mag;
 }
 
 // ---- wave-level reductions (xor butterfly: every lane ends with the same,

@@ -26,10 +26,10 @@
 // LDS; bf16 MFMA 16x16x32.
 //
 // Lane (r = l%16, q = l/16) of either kernel: B column r = weight row, A row r
-// = token row (or group row); the lane owns the contiguous quarter
-// [Q*q, Q*q + Q) of K (Q = K/4), read as 16-byte chunks of 32 elements, and
-// 32-bit word j of chunk c feeds sub-MFMA (c, j): MFMA k index 8q + i maps to
-// element Q*q + 32c + 8j + i on both operands, so the sum is over all of K.
+// = token row (or group row).  The lane's 16-byte code chunk c is bytes
+// [64c + 16q, +16) of its weight row, i.e. elements 128c + 32q + [0, 32), and
+// 32-bit word j of it feeds sub-MFMA (c, j): MFMA k index 8q + i maps to
+// element 128c + 32q + 8j + i on both operands, so the sum is over all of K.
 #include "moe_ffn_common.hpp"
 #include "moe_internal.hpp"
 
@@ -116,55 +116,40 @@ __global__ __launch_bounds__(256) void k_dec_xprep(const uint16_t* __restrict__ 
 // ------------------------------- gate_up ----------------------------------
 // One wave = one unit (group, 16 gate/up row pairs, all of K); a block holds
 // WPB waves = WPB consecutive units of one group and one LDS copy of the f16
-// activation rows.  K is split between the 4 lane groups q of the wave in
-// contiguous quarters: lane (r16, q) owns elements [Q*q, Q*q + Q) of weight row
-// r16, Q = H/4, read as 16-byte code chunks (32 elements, one 128-element step
-// per 4 chunks); its Q/16 block scales are contiguous bytes.
+// activation rows.
+//
+// Code loads are row-contiguous: lane (r16, q) reads bytes [64c + 16q, +16)
+// of weight row r16 for c = 0 .. NCH-1, so every load instruction covers 64
+// contiguous bytes of each of 16 rows (measured on the device: 4.5 TB/s for
+// this pattern against 2.7 TB/s when each lane's 16 bytes sit in a segment of
+// their own).  Word j of chunk c holds elements 128c + 32q + 8j + [0, 8),
+// block 8c + 2q + j/2.  The block scales of the unit's rows are two
+// contiguous runs (16 gate rows, 16 up rows, H/16 bytes each) and go to LDS
+// by DMA; each chunk's scale pair is read from there.
 //
 // Load order (all issued before the first wait): the group lookup, then the
-// activation rows straight into LDS (global->LDS DMA, no registers), then
-// every weight word of the unit, then the epilogue's metadata.  The LDS rows
-// are unpadded with the 16-byte chunk index XOR-swizzled by (row & 15), so
-// the A-operand reads of 16 rows at one chunk hit 16 distinct bank groups.
+// activation rows and the scale runs straight into LDS (global->LDS DMA, no
+// registers), then every code word of the unit, then the epilogue's
+// metadata.  The activation rows are unpadded with the 16-byte chunk index
+// XOR-swizzled by (row & 15), so the A-operand reads of 16 rows at one chunk
+// hit 16 distinct bank groups.
 
-// The 2*NCH contiguous block-scale bytes of a lane (2 per 32-element chunk),
-// kept as the words they were loaded as: one load of 2, 4 or 8 bytes, or
-// 16-byte loads, so no unpacking waits on the load.
-template <int NCH>
-struct ScaleWords {
-  static constexpr int kLoads = NCH >= 8 ? NCH / 8 : 1;  // load instructions issued by load()
-  uint32_t w[NCH >= 2 ? NCH / 2 : 1];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    if constexpr (NCH == 1) {
-      w[0] = *(const uint16_t*)p;
-    } else if constexpr (NCH == 2) {
-      w[0] = *(const uint32_t*)p;
-    } else if constexpr (NCH == 4) {
-      const u32x2 v = *(const u32x2*)p;
-      w[0] = v.x;
-      w[1] = v.y;
-    } else {
+// Copy BYTES contiguous bytes (a multiple of 256) from global memory to LDS
+// with one wave: 16 bytes per lane when BYTES is a multiple of 1 KB, else 4.
+template <int BYTES>
+__device__ __forceinline__ void dma_run(const uint8_t* g, uint8_t* lds, int lane) {
+  static_assert(BYTES % 256 == 0, "whole DMA instructions");
+  if constexpr (BYTES % 1024 == 0) {
 #pragma unroll
-      for (int i = 0; i < NCH / 8; ++i) {
-        const u32x4 v = *(const u32x4*)(p + 16 * i);
-        w[4 * i] = v.x;
-        w[4 * i + 1] = v.y;
-        w[4 * i + 2] = v.z;
-        w[4 * i + 3] = v.w;
-      }
-    }
+    for (int i = 0; i < BYTES / 1024; ++i) dma16(g + 1024 * i + 16 * lane, lds + 1024 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < BYTES / 256; ++i)
+      __builtin_amdgcn_global_load_lds(g + 256 * i + 4 * lane,
+                                       (__attribute__((address_space(3))) void*)(lds + 256 * i), 4,
+                                       0, 0);
   }
-  // scale bytes 2c (low) and 2c+1 of the run
-  __device__ __forceinline__ uint32_t pair(int c) const {
-    return NCH == 1 ? w[0] : ((c & 1) ? (w[c / 2] >> 16) : (w[c / 2] & 0xFFFFu));
-  }
-};
-
-template <int NCH>   // NCH = 16-byte code chunks per lane per row = H / 128
-struct GURegs {
-  u32x4 g[NCH], u[NCH];
-  ScaleWords<NCH> sg, su;
-};
+}
 
 // Copy rows [0, nrows) of a row-major matrix of 16-bit values (row length
 // cpr 16-byte chunks, cpr >= 16) into LDS, chunk ch of row r stored at chunk
@@ -198,6 +183,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // TR = activation rows staged (T rounded up to 1, 2, 4 or 8; rows >= T repeat
 // row T-1), which makes the number of DMA instructions per wave a constant.
+// Dynamic LDS: [TR][H] f16 activation rows, then per wave the gate and up
+// scale runs (2 x 16 x H/16 bytes).
 template <int NCH, int WPB, int TR>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_gate_up(
     const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
@@ -205,19 +192,20 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* __restrict__ unmul, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ groups, int T, int K,
     int H, int I, int has_shared, uint16_t* __restrict__ h) {
-  extern __shared__ __align__(16) _Float16 xl[];  // [TR][H] f16, chunks swizzled
+  extern __shared__ __align__(16) _Float16 xl[];
   constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
   constexpr int NDMA = (TR * CPR + 64 * WPB - 1) / (64 * WPB);
+  constexpr int SRUN = 128 * NCH;                   // scale bytes of 16 rows
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
-  const int Q = H / 4;
   const int nbk = I / 16 / WPB;
   const int a = blockIdx.x / nbk, pb = (blockIdx.x % nbk) * WPB + wv;
   // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
   if (a >= nact) return;      // uniform per block, before any load is in flight
+  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + (size_t)wv * 2 * SRUN;
 
-  // (1) activation rows -> LDS
+  // (1) activation rows and the unit's scale runs -> LDS
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int base = 64 * (wv + WPB * i), L = base + lane;
@@ -226,29 +214,33 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       dma16(xh + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
     }
   }
+  const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
+  {
+    const uint8_t* sg = gu_scales + grow * (H / 16);
+    dma_run<SRUN>(sg, sl, lane);
+    dma_run<SRUN>(sg + (size_t)I * (H / 16), sl + SRUN, lane);
+  }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the DMA
 
-  // (2) every weight word of the unit: 2*NCH 16-byte code loads (+ scales)
-  GURegs<NCH> w;
+  // (2) every code word of the unit: 2*NCH row-contiguous 16-byte loads
+  u32x4 wg[NCH], wu[NCH];
   {
-    const size_t rowb = (size_t)H / 2, srow = (size_t)H / 16;
-    const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16 + r16;
-    const uint8_t* cg = gu_codes + grow * rowb + (size_t)(Q / 2) * q;
+    const size_t rowb = (size_t)H / 2;
+    const uint8_t* cg = gu_codes + (grow + r16) * rowb + 16 * q;
     const uint8_t* cu = cg + (size_t)I * rowb;
-    const uint8_t* sg = gu_scales + grow * srow + (size_t)(Q / 16) * q;
-    const uint8_t* su = sg + (size_t)I * srow;
-    w.sg.load(sg);
-    w.su.load(su);
+    // issued in the order the MFMAs consume them (the vector-memory counter
+    // completes in issue order, so each chunk waits only for its own words)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      w.g[c] = *(const u32x4*)(cg + 16 * c);
-      w.u[c] = *(const u32x4*)(cu + 16 * c);
+      wg[c] = *(const u32x4*)(cg + 64 * c);
+      wu[c] = *(const u32x4*)(cu + 64 * c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // (3) the epilogue's metadata; the slot of position `lane` is loaded for
-  // every lane (clamped into the group, n >= 1), so the loads after the DMA
-  // number at least 2*NCH + 3 on every path
+  // every lane (clamped into the group, n >= 1), so at least 2*NCH + 1 vector
+  // loads follow the DMA on every path
   const int p0 = offsets[e], n = offsets[e + 1] - p0;
   const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
   float ums[8];  // unmul has T <= 8 entries in a 256-byte aligned region
@@ -257,7 +249,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   const int slot_l = sorted_slot[p0 + (lane < n ? lane : n - 1)];
 
   // (4) this wave's DMA is complete once at most the 2*NCH youngest loads are
-  // outstanding; the barrier then covers the whole block.  The weight chunks
+  // outstanding; the barrier then covers the whole block.  The code chunks
   // are waited for one by one as the MFMAs reach them.
   wait_vmcnt<2 * NCH>();
   __builtin_amdgcn_s_barrier();
@@ -265,16 +257,17 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // A row r16 of the MFMA = token r16; rows >= T read row T-1 (never stored)
   const int xr = r16 < T ? r16 : T - 1;
   const uint8_t* xrow = (const uint8_t*)xl;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
   f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const f16x2 sgv = e4m3x2_to_f16(w.sg.pair(c));
-    const f16x2 suv = e4m3x2_to_f16(w.su.pair(c));
+    const f16x2 sgv = e4m3x2_to_f16(*(const uint16_t*)(srow + 8 * c));
+    const f16x2 suv = e4m3x2_to_f16(*(const uint16_t*)(srow + SRUN + 8 * c));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f16x8 av = *(const f16x8*)(xrow + swz_off(xr, (Q / 8) * q + 4 * c + j, CPR));
-      dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w.g[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
-      du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w.u[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
+      const f16x8 av = *(const f16x8*)(xrow + swz_off(xr, 16 * c + 4 * q + j, CPR));
+      dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wg[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
+      du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wu[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -301,49 +294,49 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 // One wave = one unit (group, 64 output rows as 4 MFMA blocks of 16, all of
 // K = I); a block holds WPB consecutive units of one group and the group's h
 // rows (up to 16 per pass) in LDS, chunk-swizzled like the activations above.
-// Lane (r16, q) owns K elements [Q*q, Q*q + Q), Q = I/4, as 16-byte code
-// chunks; its Q/16 scale bytes are contiguous.  Every position of a group's
-// range is a valid slot (the permutation only places valid ones), so the rows
-// are read without a slot lookup; rows of a pass past the group's end repeat
-// its last row and are not stored.
-
-template <int NCH>   // NCH = I / 128
-struct DNRegs {
-  u32x4 c[4][NCH];
-  ScaleWords<NCH> s[4];
-};
-
-template <int NCH, int WPB>
+// Code loads are row-contiguous as in gate_up (lane (r16, q), chunk c: bytes
+// 64c + 16q of the row); the 64 rows' block scales are one contiguous run
+// that goes to LDS by DMA.  Every position of a group's range is a valid slot
+// (the permutation only places valid ones), so the rows are read without a
+// slot lookup; rows of a pass past the group's end repeat its last row and
+// are not stored.
+// Dynamic LDS: [16][I] bf16 h rows, then per wave the scale run (64 x I/16 B).
+template <int NCH, int WPB>   // NCH = I / 128
 __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
     const float* __restrict__ scale2, const uint16_t* __restrict__ h,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ groups, int H, int I,
     uint16_t* __restrict__ y) {
-  extern __shared__ __align__(16) uint16_t hl[];  // [16][I] bf16, chunks swizzled
+  extern __shared__ __align__(16) uint16_t hl[];
+  constexpr int SRUN = 512 * NCH;  // scale bytes of 64 rows
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
-  const int Q = I / 4, cpr = I / 8;
+  const int cpr = I / 8;
   const int nbk = H / 64 / WPB;
   const int a = blockIdx.x / nbk, rb = (blockIdx.x % nbk) * WPB + wv;
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // both lookups in one trip
   if (a >= nact) return;      // uniform per block
-  DNRegs<NCH> w;
+  uint8_t* sl = (uint8_t*)hl + (size_t)16 * I * 2 + (size_t)wv * SRUN;
+  const size_t row0 = (size_t)e * H + (size_t)rb * 64;
+  dma_run<SRUN>(dn_scales + row0 * (I / 16), sl, lane);
+  asm volatile("" ::: "memory");
+  u32x4 w[4][NCH];
   {
-    const size_t rowb = (size_t)I / 2, srow = (size_t)I / 16;
+    const size_t rowb = (size_t)I / 2;
+    const uint8_t* cr = dn_codes + (row0 + r16) * rowb + 16 * q;
+    // issued chunk by chunk, the order the MFMAs consume them
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const size_t row = (size_t)e * H + (size_t)rb * 64 + nb * 16 + r16;
-      const uint8_t* cr = dn_codes + row * rowb + (size_t)(Q / 2) * q;
-      const uint8_t* sr = dn_scales + row * srow + (size_t)(Q / 16) * q;
+    for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) w.c[nb][c] = *(const u32x4*)(cr + 16 * c);
-      w.s[nb].load(sr);
+      for (int nb = 0; nb < 4; ++nb) w[nb][c] = *(const u32x4*)(cr + (size_t)nb * 16 * rowb + 64 * c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   asm volatile("" ::: "memory");  // the group's row range is looked up after the weights are requested
   const int p0 = offsets[e], n = offsets[e + 1] - p0;
   const float s2d = scale2[3 * e + 2];
   const uint8_t* hrow = (const uint8_t*)hl;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
   // rows [r0, r0 + 16) of the group: stage, multiply, store
   auto pass = [&](int r0) {
     const int last = (n - r0 < 16 ? n - r0 : 16) - 1;
@@ -356,19 +349,17 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      float sc[4][2];
+      f32x2 sc[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint32_t sp = w.s[nb].pair(c);
-        sc[nb][0] = e4m3_to_f32(sp & 0xFFu);
-        sc[nb][1] = e4m3_to_f32((sp >> 8) & 0xFFu);
-      }
+      for (int nb = 0; nb < 4; ++nb)
+        sc[nb] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
+            *(const uint16_t*)(srow + nb * 16 * (8 * NCH) + 8 * c), 1.0f, false);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(hrow + swz_off(r16, (Q / 8) * q + 4 * c + j, cpr)));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(hrow + swz_off(r16, 16 * c + 4 * q + j, cpr)));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dq8(w.c[nb][c][j], sc[nb][j >> 1]), acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dq8(w[nb][c][j], j < 2 ? sc[nb].x : sc[nb].y), acc[nb], 0, 0, 0);
       }
       // keep each chunk's dequantised operands next to their MFMAs (bounds
       // the registers in flight)
@@ -390,15 +381,12 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   pass(0);
   for (int r0 = 16; r0 < n; r0 += 16) {  // only when ids repeat (> 16 rows)
     __syncthreads();  // previous pass done reading hl
-    // the weight words count as redefined on every pass, so the dequantised
+    // the code words count as redefined on every pass, so the dequantised
     // operands (4x the registers of the codes) are not hoisted out of the loop
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w.c[nb][c]));
-#pragma unroll
-      for (int c = 0; c < (NCH >= 2 ? NCH / 2 : 1); ++c) asm volatile("" : "+v"(w.s[nb].w[c]));
-    }
+      for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w[nb][c]));
     pass(r0);
   }
 }
@@ -475,7 +463,7 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const int wpb_g = gu_units >= 8 * cus ? 4 : 1;
   const int wpb_d = dn_units >= 8 * cus ? 4 : 1;
   const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
-  const size_t lds_gu = (size_t)tr * H * sizeof(_Float16);
+  const size_t lds_gu = (size_t)tr * H * sizeof(_Float16) + (size_t)wpb_g * 2 * 16 * (H / 16);
   const dim3 blk(256);
   const dim3 g1((unsigned)(gu_units / wpb_g)), b1(64 * wpb_g);
   const int nch = H / 128;
@@ -503,7 +491,7 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
 #undef MOE_DEC_GU1
 #undef MOE_DEC_GU
   const dim3 g2((unsigned)(dn_units / wpb_d)), b2(64 * wpb_d);
-  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t);
+  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)wpb_d * 64 * (I / 16);
   const int ncd = I / 128;
 #define MOE_DEC_DN(NCH)                                                                            \
   do {                                                                                             \

@@ -102,6 +102,9 @@ __device__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT,
   return true;
 }
 
+// s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -130,14 +133,16 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
                                         uint16_t* __restrict__ out) {
   constexpr int NTHR = 64 * NW;
   constexpr int WR = 64 * NW;           // weight rows of a tile
-  constexpr int ACH = kPM * 16 / NTHR;  // A 16-byte chunks per thread per step
-  constexpr int WCH = WR * 4 / NTHR;    // weight 16-byte chunks per thread per step
-  static_assert(WCH == 4, "4 weight chunks per thread");
+  static_assert(NMB * 32 * 256 % (1024 * NW) == 0, "whole A DMA instructions per wave");
   const int KD = GU ? H : I;  // reduction length
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = ti.g;
 
-  // ---- per-thread load addresses (fixed across K steps) ----
+  // ---- per-lane DMA sources (fixed across K steps) ----
+  // Wave wv moves LDS bytes [1024*(wv + NW*i), +1024) of the A and W stages
+  // and [256*(wv + NW*i), +256) of the S stage with one global->LDS DMA
+  // instruction each; lane l's bytes land at 16*l (4*l for S), so the lane
+  // fetches the global chunk that belongs at that (swizzled) position.
   const size_t rowb = (size_t)KD / 2, srow = (size_t)KD / 16;
   auto wrow = [&](int rho) -> size_t {  // global weight row of tile row rho
     if (GU) {
@@ -147,39 +152,43 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
     }
     return (size_t)e * H + (size_t)ti.nt * WR + rho;
   };
-  const uint8_t* wsrc[WCH];
-  int wdst[WCH];
+  constexpr int AI = NMB * 32 * 256 / 1024 / NW;  // A DMA instructions per wave per step (valid row blocks only)
+  constexpr int WI = WR * 64 / 1024 / NW;    // = 4 weight DMA instructions
+  constexpr int SI = WR * 8 / 256 / NW;      // = 2 scale DMA instructions (4 bytes per lane)
+  const uint8_t* asrc_p[AI];
+  const uint8_t* wsrc[WI];
+  const uint8_t* ssrc[SI];
 #pragma unroll
-  for (int j = 0; j < WCH; ++j) {
-    const int L = tid + NTHR * j, rho = L >> 2, cp = L & 3;
-    wsrc[j] = codes + wrow(rho) * rowb + 16 * cp;
-    wdst[j] = rho * 64 + 16 * (cp ^ ((rho >> 2) & 3));
+  for (int i = 0; i < AI; ++i) {
+    const int L = 64 * (wv + NW * i) + lane, r = L >> 4, chp = L & 15;
+    asrc_p[i] = (const uint8_t*)(asrc + (size_t)sm.row_src[r] * KD) + 16 * (chp ^ (r & 15));
   }
-  const uint8_t* ssrc = scales + wrow(tid) * srow;  // WR == NTHR rows: one per thread
-  const uint8_t* asrc_p[ACH];
-  int adst[ACH];
 #pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int L = tid + NTHR * j, r = L >> 4, ch = L & 15;
-    asrc_p[j] = (const uint8_t*)(asrc + (size_t)sm.row_src[r] * KD) + 16 * ch;
-    adst[j] = r * 256 + 16 * (ch ^ (r & 15));
+  for (int i = 0; i < WI; ++i) {
+    const int L = 64 * (wv + NW * i) + lane, rho = L >> 2, cpp = L & 3;
+    wsrc[i] = codes + wrow(rho) * rowb + 16 * (cpp ^ ((rho >> 2) & 3));
   }
-
-  u32x4 ra[ACH], rw[WCH];
-  u32x2 rs;
-  auto load_step = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) ra[j] = *(const u32x4*)(asrc_p[j] + 256 * s);
+  for (int i = 0; i < SI; ++i) {
+    const int L = 64 * (wv + NW * i) + lane;
+    ssrc[i] = scales + wrow(L >> 1) * srow + 4 * (L & 1);
+  }
+  auto dma_step = [&](int s, int st) {
 #pragma unroll
-    for (int j = 0; j < WCH; ++j) rw[j] = *(const u32x4*)(wsrc[j] + 64 * s);
-    rs = *(const u32x2*)(ssrc + 8 * s);
-  };
-  auto store_step = [&](int st) {
+    for (int i = 0; i < AI; ++i)
+      __builtin_amdgcn_global_load_lds(asrc_p[i] + 256 * s,
+                                       (__attribute__((address_space(3))) void*)&sm.As[st][1024 * (wv + NW * i)],
+                                       16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) *(u32x4*)(&sm.As[st][adst[j]]) = ra[j];
+    for (int i = 0; i < WI; ++i)
+      __builtin_amdgcn_global_load_lds(wsrc[i] + 64 * s,
+                                       (__attribute__((address_space(3))) void*)&sm.Ws[st][1024 * (wv + NW * i)],
+                                       16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < WCH; ++j) *(u32x4*)(&sm.Ws[st][wdst[j]]) = rw[j];
-    *(u32x2*)(&sm.Ss[st][tid * 8]) = rs;
+    for (int i = 0; i < SI; ++i)
+      __builtin_amdgcn_global_load_lds(ssrc[i] + 8 * s,
+                                       (__attribute__((address_space(3))) void*)&sm.Ss[st][256 * (wv + NW * i)],
+                                       4, 0, 0);
   };
 
   const int n32 = lane & 31, q = lane >> 5;
@@ -194,12 +203,13 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
 
   const int nsteps = KD / kPK;
-  load_step(0);
-  store_step(0);
+  dma_step(0, 0);
+  wait_vmcnt0();
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int st = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
+    // stage st ^ 1 was last read in step s - 1, which every wave has finished
+    if (s + 1 < nsteps) dma_step(s + 1, st ^ 1);
     const uint8_t* A = sm.As[st];
     const uint8_t* Wt = sm.Ws[st];
     const uint8_t* St = sm.Ss[st];
@@ -215,48 +225,57 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
         wc[c][nb] = *(const u32x4*)(Wt + rho * 64 + 16 * (cp ^ ((rho >> 2) & 3)));
       }
     }
+    // this lane's two block scales of chunk c: bytes 4c + 2q, 4c + 2q + 1
+    uint32_t sp[2][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      // this lane's two block scales of chunk c: bytes 4c + 2q, 4c + 2q + 1
-      uint32_t sp[2];
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sp[nb] = q ? (sw[nb][c] >> 16) : sw[nb][c];
+      for (int nb = 0; nb < 2; ++nb) sp[c][nb] = q ? (sw[nb][c] >> 16) : sw[nb][c];
+    // the A operands of sub-step t = 4c + wd are read one sub-step ahead
+    auto read_a = [&](int t, u32x4 (&av)[NMB]) {
+      const int ach = 8 * (t >> 2) + 4 * q + (t & 3);
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const int ach = 8 * c + 4 * q + wd;
-        u32x4 av[NMB];
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int r = 32 * mb + n32;
+        av[mb] = *(const u32x4*)(A + r * 256 + 16 * (ach ^ (r & 15)));
+      }
+    };
+    u32x4 av_cur[NMB], av_nxt[NMB];
+    read_a(0, av_cur);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const int r = 32 * mb + n32;
-          av[mb] = *(const u32x4*)(A + r * 256 + 16 * (ach ^ (r & 15)));
-        }
-        u32x4 b[2];
+    for (int t = 0; t < 8; ++t) {
+      const int c = t >> 2, wd = t & 3;
+      if (t < 7) read_a(t + 1, av_nxt);
+      u32x4 b[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          if (GU) {
-            const f16x2 sv = e4m3x2_to_f16(sp[nb]);
-            b[nb] = __builtin_bit_cast(u32x4, dqh8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
-          } else {
-            const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[nb], 1.0f, false);
-            b[nb] = __builtin_bit_cast(u32x4, dq8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            if (GU)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  as_f16x8(av[mb]), as_f16x8(b[nb]), acc[mb][nb], 0, 0, 0);
-            else
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  as_bf16x8(av[mb]), as_bf16x8(b[nb]), acc[mb][nb], 0, 0, 0);
-          }
+      for (int nb = 0; nb < 2; ++nb) {
+        if (GU) {
+          const f16x2 sv = e4m3x2_to_f16(sp[c][nb]);
+          b[nb] = __builtin_bit_cast(u32x4, dqh8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+        } else {
+          const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[c][nb], 1.0f, false);
+          b[nb] = __builtin_bit_cast(u32x4, dq8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
         }
       }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          if (GU)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                as_f16x8(av_cur[mb]), as_f16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+          else
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(av_cur[mb]), as_bf16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+        }
+      }
+      if (t < 7) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) av_cur[mb] = av_nxt[mb];
+      }
     }
-    if (s + 1 < nsteps) store_step(st ^ 1);
-    __syncthreads();
+    wait_vmcnt0();     // this wave's DMA of step s + 1 has landed
+    __syncthreads();   // ... and every wave's; stage st is free again
   }
 
   // ---- epilogue ----
