@@ -39,7 +39,7 @@ size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_m
   const size_t S = (size_t)T * K + (has_shared ? (size_t)T : 0);
   size_t b = align256(S * I * sizeof(uint16_t));
   if (act_mode == MOE_ACT_FP8_ROW) b += align256((size_t)T * H) + align256((size_t)T * sizeof(float));
-  return b + decode_workspace_extra(T, H);
+  return b + xprep_workspace_bytes(T, H);
 }
 
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
@@ -61,7 +61,7 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
     wp += align256((size_t)T * sizeof(float));
   }
   if (T <= kDecodeMaxT && decode_supported(H, I))
-    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, fp8, hbuf, xq, xs, wp, y, s);
+    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, fp8, hbuf, xq, xs, y, s);
   _Float16* xh = (_Float16*)wp;
   float* rowfac = (float*)(wp + align256((size_t)T * H * sizeof(_Float16)));
   hipError_t e = launch_xprep(x, T, H, fp8, xh, rowfac, xq, xs, s);

@@ -10,10 +10,12 @@
 // waves per CU then keep HBM busy; a block holds 1 wave when the units would
 // not fill the chip and 4 (one LDS copy of the activations) when they would.
 //
-// k_dec_xprep, once per layer call: each token row of x becomes f16 with a
-// power-of-two shift (bf16 arm; the shift is undone in the f32 epilogue, see
-// f16_row_shift) or, for the FP8 arm, is quantised to e4m3 per row and kept as
-// the (exact) f16 value of each code, with the row scale as epilogue factor.
+// k_dec_xprep (the grouped-GEMM path's activation prep, one block per token
+// row): each row of x becomes f16 with a power-of-two shift (bf16 arm; the
+// shift is undone in the f32 epilogue, see f16_row_shift) or, for the FP8 arm,
+// is quantised to e4m3 per row and kept as the (exact) f16 value of each code,
+// with the row scale as epilogue factor.  The decode path applies the same
+// rule inside k_dec_gate_up, on the rows it has staged in LDS.
 //
 // k_dec_gate_up: unit = (active group, 16 gate/up row pairs).  The MFMA runs
 // over the rows of ALL T tokens (T <= 8 of its 16 rows) and the epilogue keeps
@@ -30,6 +32,8 @@
 // [64c + 16q, +16) of its weight row, i.e. elements 128c + 32q + [0, 32), and
 // 32-bit word j of it feeds sub-MFMA (c, j): MFMA k index 8q + i maps to
 // element 128c + 32q + 8j + i on both operands, so the sum is over all of K.
+#include <type_traits>
+
 #include "moe_ffn_common.hpp"
 #include "moe_internal.hpp"
 
@@ -183,13 +187,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // TR = activation rows staged (T rounded up to 1, 2, 4 or 8; rows >= T repeat
 // row T-1), which makes the number of DMA instructions per wave a constant.
-// Dynamic LDS: [TR][H] f16 activation rows, then per wave the gate and up
-// scale runs (2 x 16 x H/16 bytes).
-template <int NCH, int WPB, int TR>
+// Dynamic LDS: [TR][H] activation rows (bf16 as loaded, f16 after the in-place
+// conversion), 8 row factors, then per wave the gate and up scale runs
+// (2 x 16 x H/16 bytes).
+//
+// The activation rows are turned into the f16 MFMA operand in LDS, in place,
+// by the block itself (the rule of k_dec_xprep, bit for bit): wave wv converts
+// rows wv, wv + WPB, ...; the row's epilogue factor goes to LDS.  With FP8,
+// block 0 also writes the row codes and scales to xq / xs.
+template <int NCH, int WPB, int TR, bool FP8>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_gate_up(
     const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
-    const float* __restrict__ scale2, const _Float16* __restrict__ xh,
-    const float* __restrict__ unmul, const int32_t* __restrict__ offsets,
+    const float* __restrict__ scale2, const uint16_t* __restrict__ x,
+    uint8_t* __restrict__ xq, float* __restrict__ xs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ groups, int T, int K,
     int H, int I, int has_shared, uint16_t* __restrict__ h) {
   extern __shared__ __align__(16) _Float16 xl[];
@@ -203,15 +213,16 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
   if (a >= nact) return;      // uniform per block, before any load is in flight
-  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + (size_t)wv * 2 * SRUN;
+  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
+  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
 
-  // (1) activation rows and the unit's scale runs -> LDS
+  // (1) activation rows (bf16) and the unit's scale runs -> LDS
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int base = 64 * (wv + WPB * i), L = base + lane;
     if (L < TR * CPR) {
       const int r = L / CPR, ch = (L % CPR) ^ (r & 15);
-      dma16(xh + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
+      dma16(x + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
     }
   }
   const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
@@ -243,9 +254,6 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // loads follow the DMA on every path
   const int p0 = offsets[e], n = offsets[e + 1] - p0;
   const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
-  float ums[8];  // unmul has T <= 8 entries in a 256-byte aligned region
-#pragma unroll
-  for (int t = 0; t < 8; ++t) ums[t] = unmul[t];
   const int slot_l = sorted_slot[p0 + (lane < n ? lane : n - 1)];
 
   // (4) this wave's DMA is complete once at most the 2*NCH youngest loads are
@@ -253,6 +261,73 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // are waited for one by one as the MFMAs reach them.
   wait_vmcnt<2 * NCH>();
   __builtin_amdgcn_s_barrier();
+
+  // (5) activation rows -> f16 in place (LDS only; the barrier that follows
+  // waits for LDS traffic, not for the code loads in flight)
+  // Two passes over the row in LDS (absmax, then convert), one chunk in
+  // registers at a time: the code words in flight keep their registers.
+  for (int r = wv; r < TR; r += WPB) {
+    float amax = 0.f;
+    for (int ch = lane; ch < CPR; ch += 64) {
+      const u32x4 v = *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+      }
+    }
+    amax = wave_max(amax);
+    float mul, rf;
+    if (FP8) {
+      rf = amax > 0.f ? amax / 448.0f : 1.0f;
+      mul = amax > 0.f ? 448.0f / amax : 1.0f;
+    } else {
+      const int sh = f16_row_shift(amax);
+      mul = ldexpf(1.0f, sh);
+      rf = ldexpf(1.0f, -sh);
+    }
+    const bool wr = FP8 && blockIdx.x == 0 && r < T;
+    if (lane == 0) {
+      fac[r] = rf;
+      if (wr) xs[r] = rf;
+    }
+    for (int ch = lane; ch < CPR; ch += 64) {
+      uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
+      const u32x4 v = *(const u32x4*)pch;
+      u32x4 o;
+      if (FP8) {
+        u32x2 code;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float f0 = bf16_bits_to_f32(v[2 * j] & 0xFFFFu) * mul;
+          float f1 = bf16_bits_to_f32(v[2 * j] >> 16) * mul;
+          float f2 = bf16_bits_to_f32(v[2 * j + 1] & 0xFFFFu) * mul;
+          float f3 = bf16_bits_to_f32(v[2 * j + 1] >> 16) * mul;
+          f0 = fminf(fmaxf(f0, -448.f), 448.f);
+          f1 = fminf(fmaxf(f1, -448.f), 448.f);
+          f2 = fminf(fmaxf(f2, -448.f), 448.f);
+          f3 = fminf(fmaxf(f3, -448.f), 448.f);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
+          code[j] = (uint32_t)w;
+        }
+        if (wr) *(u32x2*)(xq + (size_t)r * H + 8 * ch) = code;
+        const u32x2 lo = fp8x4_to_f16(code.x), hi = fp8x4_to_f16(code.y);
+        o = u32x4{lo.x, lo.y, hi.x, hi.y};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xFFFFu) * mul,
+                            bf16_bits_to_f32(v[j] >> 16) * mul);
+      }
+      *(u32x4*)pch = o;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  float ums[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ums[t] = fac[t < TR ? t : TR - 1];
 
   // A row r16 of the MFMA = token r16; rows >= T read row T-1 (never stored)
   const int xr = r16 < T ? r16 : T - 1;
@@ -316,34 +391,43 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // both lookups in one trip
   if (a >= nact) return;      // uniform per block
+  const int p0 = offsets[e], n = offsets[e + 1] - p0;  // scalar loads, in flight meanwhile
   uint8_t* sl = (uint8_t*)hl + (size_t)16 * I * 2 + (size_t)wv * SRUN;
   const size_t row0 = (size_t)e * H + (size_t)rb * 64;
-  dma_run<SRUN>(dn_scales + row0 * (I / 16), sl, lane);
-  asm volatile("" ::: "memory");
+  const size_t rowb = (size_t)I / 2;
+  const uint8_t* cr = dn_codes + (row0 + r16) * rowb + 16 * q;
   u32x4 w[4][NCH];
-  {
-    const size_t rowb = (size_t)I / 2;
-    const uint8_t* cr = dn_codes + (row0 + r16) * rowb + 16 * q;
-    // issued chunk by chunk, the order the MFMAs consume them
+  // chunks [c0, c1) of every row block, issued in the order the MFMAs use them
+  auto load_codes = [&](auto c0t, auto c1t) {
+    constexpr int c0 = decltype(c0t)::value, c1 = decltype(c1t)::value;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = c0; c < c1; ++c) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) w[nb][c] = *(const u32x4*)(cr + (size_t)nb * 16 * rowb + 64 * c);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  asm volatile("" ::: "memory");  // the group's row range is looked up after the weights are requested
-  const int p0 = offsets[e], n = offsets[e + 1] - p0;
-  const float s2d = scale2[3 * e + 2];
-  const uint8_t* hrow = (const uint8_t*)hl;
-  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
-  // rows [r0, r0 + 16) of the group: stage, multiply, store
-  auto pass = [&](int r0) {
+  };
+  // h rows [r0, r0 + 16) of the group -> LDS (rows past the end repeat the last)
+  auto stage = [&](int r0) {
     const int last = (n - r0 < 16 ? n - r0 : 16) - 1;
     dma_rows_swizzled(hl, 16, cpr, wv, WPB, lane, [&](int r) {
       return (const uint8_t*)(h + (size_t)(p0 + r0 + (r < last ? r : last)) * I);
     });
-    __syncthreads();
+  };
+  constexpr int NH = NCH / 2;  // chunks requested before the h rows
+  // Issue order: scale run, first half of the codes, h rows of the first
+  // pass, second half of the codes.  The first wait then leaves only the
+  // second half outstanding.
+  dma_run<SRUN>(dn_scales + row0 * (I / 16), sl, lane);
+  load_codes(std::integral_constant<int, 0>(), std::integral_constant<int, NH>());
+  stage(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);  // the second half stays behind the h rows
+  load_codes(std::integral_constant<int, NH>(), std::integral_constant<int, NCH>());
+  const float s2d = scale2[3 * e + 2];
+  const uint8_t* hrow = (const uint8_t*)hl;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  auto compute = [&](int r0) {
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -375,19 +459,22 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
       }
     }
   };
-  // The first pass is straight-line code: a loop whose body reads the weight
-  // registers would first wait for every outstanding load, and the h rows must
-  // be requested before that wait.
-  pass(0);
+  // this wave's DMAs are complete once only the second half of the codes is
+  // outstanding; the barrier covers the block
+  wait_vmcnt<4 * (NCH - NH)>();
+  __builtin_amdgcn_s_barrier();
+  compute(0);
   for (int r0 = 16; r0 < n; r0 += 16) {  // only when ids repeat (> 16 rows)
     __syncthreads();  // previous pass done reading hl
+    stage(r0);
+    __syncthreads();
     // the code words count as redefined on every pass, so the dequantised
     // operands (4x the registers of the codes) are not hoisted out of the loop
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w[nb][c]));
-    pass(r0);
+    compute(r0);
   }
 }
 
@@ -396,20 +483,24 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 void register_decode_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_dec_xprep<false>);
   k.push_back((const void*)&k_dec_xprep<true>);
-#define MOE_REG_GU(NCH)                                  \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 1>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 2>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 4>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 1, 8>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 1>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 2>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 4>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, 4, 8>);
+#define MOE_REG_GU3(NCH, WPB, TR)                                \
+  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, false>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, true>);
+#define MOE_REG_GU2(NCH, WPB) \
+  MOE_REG_GU3(NCH, WPB, 1)    \
+  MOE_REG_GU3(NCH, WPB, 2)    \
+  MOE_REG_GU3(NCH, WPB, 4)    \
+  MOE_REG_GU3(NCH, WPB, 8)
+#define MOE_REG_GU(NCH) \
+  MOE_REG_GU2(NCH, 1)   \
+  MOE_REG_GU2(NCH, 4)
   MOE_REG_GU(2)
   MOE_REG_GU(4)
   MOE_REG_GU(8)
   MOE_REG_GU(16)
 #undef MOE_REG_GU
+#undef MOE_REG_GU2
+#undef MOE_REG_GU3
   k.push_back((const void*)&k_dec_down<1, 1>);
   k.push_back((const void*)&k_dec_down<1, 4>);
   k.push_back((const void*)&k_dec_down<2, 1>);
@@ -440,55 +531,64 @@ hipError_t launch_xprep(const uint16_t* x, int T, int H, bool fp8, _Float16* xh,
   return hipGetLastError();
 }
 
-// f16 activation rows [T][H] and their epilogue factors [T].
-size_t decode_workspace_extra(int T, int H) {
+// f16 activation rows [T][H] and their epilogue factors [T] (grouped path).
+size_t xprep_workspace_bytes(int T, int H) {
   return align256((size_t)T * H * sizeof(_Float16)) + align256((size_t)T * sizeof(float));
+}
+
+// gate_up launch for one (NCH, WPB): picks the staged row count and the arm.
+template <int NCH, int WPB>
+static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                               const int32_t* offsets, const int32_t* sorted_slot,
+                               const int32_t* groups, bool fp8, uint8_t* xq, float* xs,
+                               uint16_t* hbuf, dim3 grid, hipStream_t s) {
+  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
+  const size_t lds = (size_t)tr * H * 2 + 256 + (size_t)WPB * 2 * 16 * (H / 16);
+#define MOE_DEC_GU1(TR, F8)                                                                       \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR, F8>), grid, dim3(64 * WPB), lds, s,  \
+             W.gu_codes, W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, groups, T, K, H, \
+             I, hs, hbuf)
+#define MOE_DEC_GU2(TR)                \
+  do {                                 \
+    if (fp8) MOE_DEC_GU1(TR, true);    \
+    else MOE_DEC_GU1(TR, false);       \
+  } while (0)
+  if (tr == 1) MOE_DEC_GU2(1);
+  else if (tr == 2) MOE_DEC_GU2(2);
+  else if (tr == 4) MOE_DEC_GU2(4);
+  else MOE_DEC_GU2(8);
+#undef MOE_DEC_GU2
+#undef MOE_DEC_GU1
 }
 
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
                              const int32_t* groups, bool fp8, uint16_t* hbuf, uint8_t* xq,
-                             float* xs, void* dec_ws, uint16_t* y, hipStream_t s) {
+                             float* xs, uint16_t* y, hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
-  _Float16* xh = (_Float16*)dec_ws;
-  float* unmul = (float*)((uint8_t*)dec_ws + align256((size_t)T * H * sizeof(_Float16)));
-  hipError_t pe = launch_xprep(x, T, H, fp8, xh, unmul, xq, xs, s);
-  if (pe != hipSuccess) return pe;
   // Waves (units) per block: 4 when there are enough units to fill the
   // chip, else 1 so that small T still spreads over many CUs.
   const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
   const long cus = num_cus();
   const int wpb_g = gu_units >= 8 * cus ? 4 : 1;
   const int wpb_d = dn_units >= 8 * cus ? 4 : 1;
-  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
-  const size_t lds_gu = (size_t)tr * H * sizeof(_Float16) + (size_t)wpb_g * 2 * 16 * (H / 16);
-  const dim3 blk(256);
-  const dim3 g1((unsigned)(gu_units / wpb_g)), b1(64 * wpb_g);
+  const dim3 g1((unsigned)(gu_units / wpb_g));
   const int nch = H / 128;
-#define MOE_DEC_GU1(NCH, WPB, TR)                                                                    \
-  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR>), g1, b1, lds_gu, s, W.gu_codes,        \
-             W.gu_scales, W.scale2, xh, unmul, offsets, sorted_slot, groups, T, K, H, I, hs, hbuf)
-#define MOE_DEC_GU2(NCH, WPB)                   \
-  do {                                          \
-    if (tr == 1) MOE_DEC_GU1(NCH, WPB, 1);      \
-    else if (tr == 2) MOE_DEC_GU1(NCH, WPB, 2); \
-    else if (tr == 4) MOE_DEC_GU1(NCH, WPB, 4); \
-    else MOE_DEC_GU1(NCH, WPB, 8);              \
-  } while (0)
-#define MOE_DEC_GU(NCH)                       \
-  do {                                        \
-    if (wpb_g == 4) MOE_DEC_GU2(NCH, 4);      \
-    else MOE_DEC_GU2(NCH, 1);                 \
+#define MOE_DEC_GU(NCH)                                                                          \
+  do {                                                                                           \
+    if (wpb_g == 4)                                                                              \
+      launch_dec_gate_up<NCH, 4>(W, x, T, K, offsets, sorted_slot, groups, fp8, xq, xs, hbuf, g1, s); \
+    else                                                                                         \
+      launch_dec_gate_up<NCH, 1>(W, x, T, K, offsets, sorted_slot, groups, fp8, xq, xs, hbuf, g1, s); \
   } while (0)
   if (nch == 2) MOE_DEC_GU(2);
   else if (nch == 4) MOE_DEC_GU(4);
   else if (nch == 8) MOE_DEC_GU(8);
   else if (nch == 16) MOE_DEC_GU(16);
   else return hipErrorInvalidValue;
-#undef MOE_DEC_GU2
-#undef MOE_DEC_GU1
 #undef MOE_DEC_GU
   const dim3 g2((unsigned)(dn_units / wpb_d)), b2(64 * wpb_d);
   const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)wpb_d * 64 * (I / 16);

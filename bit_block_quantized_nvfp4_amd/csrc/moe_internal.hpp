@@ -67,10 +67,10 @@ hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const in
                               const int32_t* sorted_slot, const _Float16* xh, const float* rowfac,
                               uint16_t* hbuf, uint16_t* y, hipStream_t s);
 bool decode_supported(int H, int I);
-size_t decode_workspace_extra(int T, int H);
+size_t xprep_workspace_bytes(int T, int H);
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
                              const int32_t* groups, bool fp8, uint16_t* hbuf, uint8_t* xq,
-                             float* xs, void* dec_ws, uint16_t* y, hipStream_t s);
+                             float* xs, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

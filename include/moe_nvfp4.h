@@ -182,8 +182,9 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
  * Workspace contents after the call (S = T*K + T*has_shared, A(n) = n rounded
  * up to a multiple of 256): bytes [0, 2*S*I) hold h as bf16 [S][I] by sorted
  * position; with MOE_ACT_FP8_ROW the e4m3 codes [T][H] follow at byte
- * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).  The f16
- * activation rows [T][H] and their fp32 epilogue factors [T] come next.
+ * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).  Scratch for
+ * the grouped path's f16 activation rows [T][H] and their fp32 epilogue
+ * factors [T] comes next (its contents are unspecified after a call).
  */
 int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
                    const int32_t* offsets, const int32_t* sorted_slot, const int32_t* groups,
