@@ -37,6 +37,35 @@ NBANKS = 8
 NLOGITS = 16
 
 
+# rocprofv3 counter summary of the expert-FFN kernels (FETCH_SIZE + WRITE_SIZE
+# per dispatch, calibrated against a 1 GiB copy), with the hash of the decode
+# kernel sources it was measured on.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_ffn_hbm_traffic_decode_T8_prefill_T4096.md")
+DECODE_SOURCES = ["bit_block_quantized_nvfp4_amd/csrc/moe_ffn_decode.hip",
+                  "bit_block_quantized_nvfp4_amd/csrc/moe_ffn_common.hpp",
+                  "bit_block_quantized_nvfp4_amd/csrc/moe_device.hpp"]
+
+
+def measured_traffic():
+    """HBM bytes per dec_gate_up launch (T=8) from the counter summary, or None
+    if the summary is missing or the decode kernel sources changed since."""
+    import hashlib
+    import re
+
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        h = hashlib.sha256()
+        for f in DECODE_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_h = re.search(r"^decode_source_sha256_16: ([0-9a-f]{16})$", text, re.M)
+    if not m_b or not m_h or m_h.group(1) != h.hexdigest()[:16]:
+        return None
+    return int(m_b.group(1))
+
+
 def _gate_up_bytes(H, I):
     return 2 * I * H // 2 + 2 * I * H // 16
 
@@ -331,7 +360,7 @@ def main():
                    "global_batch": 8, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "dec_gate_up", "achieved": round(gu["GBs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_us": round(gu["avg_us"], 2),
+                     "traffic": measured_traffic(), "avg_us": round(gu["avg_us"], 2),
                      "bytes_per_launch": int(gu["bytes"])},
         "cpu_baseline": cpu,
         "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "us_eager": round(head["ms_eager"] * 1e3, 2),
