@@ -84,7 +84,15 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g * sigma(g), sigma(g) = 1 / (1 + exp(-g)), with the hardware
+// v_exp_f32 (2^x) and v_rcp_f32 (each ~1 ulp in f32): the result is rounded
+// to bf16 (2^-9 relative) right after, so correctly rounded exp and division
+// would buy nothing.  Finite g far below zero gives -0 (exp2 overflows to
+// +inf and rcp(+inf) = 0); g far above zero gives g.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Token of a sorted slot: routed slot s -> s / K, shared slot T*K + t -> t,
 // anything else -> -1 (the row is skipped).
