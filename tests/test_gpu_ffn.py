@@ -108,11 +108,25 @@ def test_fp8_arm(moe, cfg):
     assert np.array_equal(q, qo)
 
 
-def test_fp8_zero_rows(moe):
-    wl = make_workload("z", T=12, H=256, E=8, K=2, I=128, has_shared=True, seed=6)
+@pytest.mark.parametrize("T", [12, 6])   # grouped path; decode path (rows converted in LDS)
+def test_fp8_zero_rows(moe, T):
+    wl = make_workload("z", T=T, H=256, E=8, K=2, I=128, has_shared=True, seed=6)
     wl.x_bf16[3] = 0
-    wl.x_bf16[7] = 0x8000          # -0.0
-    _full_check(moe, wl, act_mode=1, tag="fp8 zero rows")
+    wl.x_bf16[T - 1] = 0x8000      # -0.0
+    _full_check(moe, wl, act_mode=1, tag=f"fp8 zero rows T={T}")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=3, H=512, E=32, K=4, I=256, has_shared=True),      # decode, 4 chunks per lane
+    dict(T=7, H=1024, E=64, K=6, I=1024, has_shared=True),    # decode, 8 chunks, down with 8 chunks
+    dict(T=8, H=1024, E=16, K=8, I=128, has_shared=False),    # decode, one down chunk
+    dict(T=2, H=4096, E=8, K=2, I=128, has_shared=True),      # T <= 8 with no decode variant: grouped path
+    dict(T=5, H=1024, E=16, K=3, I=384, has_shared=True),     # I / 128 = 3: grouped path at T <= 8
+])
+def test_small_T_shapes(moe, cfg):
+    _full_check(moe, make_workload("q", seed=9, **cfg), tag=f"small T {cfg}")
+    _full_check(moe, make_workload("q", seed=10, x_kind="student_t", **cfg), act_mode=1,
+                tag=f"small T fp8 {cfg}")
 
 
 @pytest.mark.parametrize("cfg", [
