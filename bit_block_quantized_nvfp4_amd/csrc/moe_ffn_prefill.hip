@@ -38,67 +38,95 @@ constexpr int kPM = 128;   // rows per tile
 constexpr int kPK = 128;   // K per step
 constexpr int kPMaxG = 1025;
 
-__device__ __forceinline__ int pf_xcd_remap(int b, int nb) {
-  // blocks b = x, x+8, x+16, ... run on XCD x: give each XCD a contiguous run
-  // of items, so the tiles that share a weight tile (or an A tile) share its L2
-  const int q = nb / 8, r = nb % 8, xcd = b % 8, i = b / 8;
-  return (xcd < r) ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
-}
-
 struct PfTile {
   int g, p0, rows, nt;
 };
 
-// Item lookup from offsets: items are enumerated group by group, N tile by N
-// tile, row tile by row tile.  All threads must call it; false = no item.
+// Item lookup from offsets.  Items are ordered heaviest first, so the short
+// ones fill the end of the launch: class 0 holds the row tiles with 4 valid
+// 32-row blocks (every full tile, and a last tile of more than 96 rows),
+// classes 1, 2, 3 the last tiles with 3, 2, 1 valid blocks; within a class,
+// group by group, N tile by N tile, row tile by row tile.  The four per-group
+// counts are scanned at once as 16-bit fields of a 64-bit word.  All threads
+// must call it; false = no item.
+__device__ __forceinline__ unsigned long long pf_wave_incl_scan64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int pf_field(unsigned long long v, int k) {
+  return (int)((v >> (16 * k)) & 0xFFFFull);
+}
+
 template <int NTHR>
-__device__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT, int* base,
-                             int* wsum, PfTile* ti) {
+__device__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT,
+                             unsigned long long* base, unsigned long long* wsum, PfTile* ti) {
   constexpr int NWV = NTHR / 64;
   const int tid = threadIdx.x;
   for (int g = tid; g < G; g += NTHR) {
     const int cnt = offsets[g + 1] - offsets[g];
-    base[g] = cnt > 0 ? (cnt + kPM - 1) / kPM : 0;
+    const int rem = cnt % kPM;
+    const int c0 = cnt / kPM + (rem > 96 ? 1 : 0);
+    const int k = (rem > 0 && rem <= 96) ? 4 - (rem + 31) / 32 : 0;  // class of the last tile
+    base[g] = (unsigned long long)c0 | (k ? 1ull << (16 * k) : 0ull);
   }
   __syncthreads();
   const int per = (G + NTHR - 1) / NTHR;
   const int lo = min(tid * per, G), hi = min(lo + per, G);
-  int local = 0;
+  unsigned long long local = 0;
   for (int i = lo; i < hi; ++i) local += base[i];
   const int lane = tid & 63, wv = tid >> 6;
-  const int incl = wave_incl_scan(local, lane);
+  const unsigned long long incl = pf_wave_incl_scan64(local, lane);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  int before = 0, total = 0;
+  unsigned long long before = 0, total = 0;
 #pragma unroll
   for (int i = 0; i < NWV; ++i) {
-    before += (i < wv) ? wsum[i] : 0;
+    before += (i < wv) ? wsum[i] : 0ull;
     total += wsum[i];
   }
-  int run = before + incl - local;
+  unsigned long long run = before + incl - local;
   for (int i = lo; i < hi; ++i) {
-    const int v = base[i];
+    const unsigned long long v = base[i];
     base[i] = run;
     run += v;
   }
   __syncthreads();
-  const int L = pf_xcd_remap(blockIdx.x, gridDim.x);
-  if (L >= total * NT) return false;
-  // last g with base[g] * NT <= L; empty groups share the base of the next
-  // non-empty one, so the search lands on the group that owns L
+  int L = blockIdx.x, k = 0;
+  for (; k < 4; ++k) {
+    const int n = pf_field(total, k) * NT;
+    if (L < n) break;
+    L -= n;
+  }
+  if (k == 4) return false;
+  // last g with base_k[g] * NT <= L; groups with nothing in class k share the
+  // base of the next group that has, so the search lands on the owner of L
   int lo_g = 0, hi_g = G - 1;
   while (lo_g < hi_g) {
     const int mid = (lo_g + hi_g + 1) >> 1;
-    if (base[mid] * NT <= L) lo_g = mid;
+    if (pf_field(base[mid], k) * NT <= L) lo_g = mid;
     else hi_g = mid - 1;
   }
   const int g = lo_g;
-  const int mt_g = ((offsets[g + 1] - offsets[g]) + kPM - 1) / kPM;
-  const int li = L - base[g] * NT;
+  const int cnt = offsets[g + 1] - offsets[g];
+  const int li = L - pf_field(base[g], k) * NT;
+  int nt, mt;
+  if (k == 0) {
+    const int mt_g = cnt / kPM + (cnt % kPM > 96 ? 1 : 0);
+    nt = li / mt_g;
+    mt = li % mt_g;
+  } else {
+    nt = li;
+    mt = cnt / kPM;
+  }
   ti->g = g;
-  ti->nt = li / mt_g;
-  ti->p0 = offsets[g] + (li % mt_g) * kPM;
-  ti->rows = min(kPM, offsets[g + 1] - ti->p0);
+  ti->nt = nt;
+  ti->p0 = offsets[g] + mt * kPM;
+  ti->rows = min(kPM, cnt - mt * kPM);
   return true;
 }
 
@@ -115,8 +143,8 @@ struct PfSmem {
   uint8_t As[2][kPM * 256];  // A tile of a K step, 16-byte chunks swizzled by (row & 15)
   uint8_t Ws[2][WR * 64];    // weight codes of a K step, chunks swizzled by ((row >> 2) & 3)
   uint8_t Ss[2][WR * 8];     // block scales of a K step
-  int base[kPMaxG];
-  int wsum[NW];
+  unsigned long long base[kPMaxG];  // item table of pf_find_tile
+  unsigned long long wsum[NW];
   int row_src[kPM];          // GU: token of the row; DN: sorted position (valid even for padding)
   float row_fac[kPM];        // GU: epilogue factor of the row's token
   int row_ok[kPM];
