@@ -235,7 +235,7 @@ def main():
                          "prefill layer and a plain copy of COPY_BYTES (the counters' scale reference)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the expert-parallel split is a design note only).", file=sys.stderr)
         sys.exit(2)
 

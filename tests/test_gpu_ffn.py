@@ -1,7 +1,7 @@
 """GPU parity of the expert FFN (A3-A9) and the combine (A10) against the fp64
 oracle.
 
-Gates (north-star reading of "max relative error", normwise over the whole
+Gates (the reading of "max relative error" taken here: normwise over the whole
 output: max|y - y_ref| / max|y_ref|):
   * bf16 path vs the exact fp64 oracle:                    <= 2e-2
   * FP8-activation arm vs the exact fp64 oracle:           <= 6e-2
