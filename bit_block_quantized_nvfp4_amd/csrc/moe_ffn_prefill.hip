@@ -10,12 +10,13 @@
 //   down (DN):    A = bf16 h rows (contiguous sorted positions), B = NVFP4 down
 //                 rows dequantised to bf16, epilogue y = bf16(acc * s2d).
 //
-// Work item = (group, 128-row tile of its sorted rows, N tile).  A block of NW
-// waves owns 64*NW weight rows of the N tile: wave w holds two 32-row MFMA
-// blocks (GU: 32 gate rows and the 32 up rows of the same pairs; DN: rows
-// 32w and 32*NW + 32w of the tile) against all 128 tile rows (four 32-row
-// blocks, the ones past the group's end skipped).  Every weight byte is
-// dequantised exactly once per block; the A tile is shared by all waves.
+// Work item = (group, 128-row tile of its sorted rows); the block runs every
+// N tile of it in turn.  A block of NW waves owns 64*NW weight rows of an N
+// tile: wave w holds two 32-row MFMA blocks (GU: 32 gate rows and the 32 up
+// rows of the same pairs; DN: rows 32w and 32*NW + 32w of the tile) against
+// all 128 tile rows (four 32-row blocks, the ones past the group's end
+// skipped).  Every weight byte is dequantised exactly once per row tile; the
+// A tile is shared by all waves.
 //
 // K runs in steps of 128.  Each step's A tile (128 rows x 256 B), weight
 // codes (64*NW rows x 64 B) and block scales (64*NW rows x 8 B) are loaded by
@@ -157,7 +158,7 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
                                         const uint8_t* __restrict__ codes,
                                         const uint8_t* __restrict__ scales,
                                         const float* __restrict__ scale2,
-                                        const uint16_t* __restrict__ asrc, int H, int I,
+                                        const uint16_t* __restrict__ asrc, int H, int I, int NT,
                                         uint16_t* __restrict__ out) {
   constexpr int NTHR = 64 * NW;
   constexpr int WR = 64 * NW;           // weight rows of a tile
@@ -180,6 +181,9 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
     }
     return (size_t)e * H + (size_t)ti.nt * WR + rho;
   };
+  // the block runs every N tile of its row tile; N tile j is rows + j * NROWS
+  constexpr int NROWS = GU ? 32 * NW : WR;
+  const size_t nt_codes = (size_t)NROWS * rowb, nt_scales = (size_t)NROWS * srow;
   constexpr int AI = NMB * 32 * 256 / 1024 / NW;  // A DMA instructions per wave per step (valid row blocks only)
   constexpr int WI = WR * 64 / 1024 / NW;    // = 4 weight DMA instructions
   constexpr int SI = WR * 8 / 256 / NW;      // = 2 scale DMA instructions (4 bytes per lane)
@@ -201,6 +205,7 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
     const int L = 64 * (wv + NW * i) + lane;
     ssrc[i] = scales + wrow(L >> 1) * srow + 4 * (L & 1);
   }
+  int j = 0;  // N tile
   auto dma_step = [&](int s, int st) {
 #pragma unroll
     for (int i = 0; i < AI; ++i)
@@ -209,12 +214,12 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
                                        16, 0, 0);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc[i] + 64 * s,
+      __builtin_amdgcn_global_load_lds(wsrc[i] + j * nt_codes + 64 * s,
                                        (__attribute__((address_space(3))) void*)&sm.Ws[st][1024 * (wv + NW * i)],
                                        16, 0, 0);
 #pragma unroll
     for (int i = 0; i < SI; ++i)
-      __builtin_amdgcn_global_load_lds(ssrc[i] + 8 * s,
+      __builtin_amdgcn_global_load_lds(ssrc[i] + j * nt_scales + 8 * s,
                                        (__attribute__((address_space(3))) void*)&sm.Ss[st][256 * (wv + NW * i)],
                                        4, 0, 0);
   };
@@ -224,116 +229,123 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
   rho_b[0] = 32 * wv + n32;
   rho_b[1] = 32 * NW + 32 * wv + n32;
 
-  f32x16 acc[NMB][2];
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+  for (; j < NT; ++j) {
+    f32x16 acc[NMB][2];
+  #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+  #pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
 
-  const int nsteps = KD / kPK;
-  dma_step(0, 0);
-  wait_vmcnt0();
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int st = s & 1;
-    // stage st ^ 1 was last read in step s - 1, which every wave has finished
-    if (s + 1 < nsteps) dma_step(s + 1, st ^ 1);
-    const uint8_t* A = sm.As[st];
-    const uint8_t* Wt = sm.Ws[st];
-    const uint8_t* St = sm.Ss[st];
-    u32x2 sw[2];
-    u32x4 wc[2][2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int rho = rho_b[nb];
-      sw[nb] = *(const u32x2*)(St + rho * 8);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int cp = 2 * c + q;
-        wc[c][nb] = *(const u32x4*)(Wt + rho * 64 + 16 * (cp ^ ((rho >> 2) & 3)));
-      }
-    }
-    // this lane's two block scales of chunk c: bytes 4c + 2q, 4c + 2q + 1
-    uint32_t sp[2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sp[c][nb] = q ? (sw[nb][c] >> 16) : sw[nb][c];
-    // the A operands of sub-step t = 4c + wd are read one sub-step ahead
-    auto read_a = [&](int t, u32x4 (&av)[NMB]) {
-      const int ach = 8 * (t >> 2) + 4 * q + (t & 3);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const int r = 32 * mb + n32;
-        av[mb] = *(const u32x4*)(A + r * 256 + 16 * (ach ^ (r & 15)));
-      }
-    };
-    u32x4 av_cur[NMB], av_nxt[NMB];
-    read_a(0, av_cur);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int c = t >> 2, wd = t & 3;
-      if (t < 7) read_a(t + 1, av_nxt);
-      u32x4 b[2];
-#pragma unroll
+    const int nsteps = KD / kPK;
+    dma_step(0, 0);
+    wait_vmcnt0();
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int st = s & 1;
+      // stage st ^ 1 was last read in step s - 1, which every wave has finished
+      if (s + 1 < nsteps) dma_step(s + 1, st ^ 1);
+      const uint8_t* A = sm.As[st];
+      const uint8_t* Wt = sm.Ws[st];
+      const uint8_t* St = sm.Ss[st];
+      u32x2 sw[2];
+      u32x4 wc[2][2];
+  #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        if (GU) {
-          const f16x2 sv = e4m3x2_to_f16(sp[c][nb]);
-          b[nb] = __builtin_bit_cast(u32x4, dqh8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
-        } else {
-          const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[c][nb], 1.0f, false);
-          b[nb] = __builtin_bit_cast(u32x4, dq8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+        const int rho = rho_b[nb];
+        sw[nb] = *(const u32x2*)(St + rho * 8);
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int cp = 2 * c + q;
+          wc[c][nb] = *(const u32x4*)(Wt + rho * 64 + 16 * (cp ^ ((rho >> 2) & 3)));
         }
       }
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
+      // this lane's two block scales of chunk c: bytes 4c + 2q, 4c + 2q + 1
+      uint32_t sp[2][2];
+  #pragma unroll
+      for (int c = 0; c < 2; ++c)
+  #pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sp[c][nb] = q ? (sw[nb][c] >> 16) : sw[nb][c];
+      // the A operands of sub-step t = 4c + wd are read one sub-step ahead
+      auto read_a = [&](int t, u32x4 (&av)[NMB]) {
+        const int ach = 8 * (t >> 2) + 4 * q + (t & 3);
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int r = 32 * mb + n32;
+          av[mb] = *(const u32x4*)(A + r * 256 + 16 * (ach ^ (r & 15)));
+        }
+      };
+      u32x4 av_cur[NMB], av_nxt[NMB];
+      read_a(0, av_cur);
+  #pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int c = t >> 2, wd = t & 3;
+        if (t < 7) read_a(t + 1, av_nxt);
+        u32x4 b[2];
+  #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          if (GU)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                as_f16x8(av_cur[mb]), as_f16x8(b[nb]), acc[mb][nb], 0, 0, 0);
-          else
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(av_cur[mb]), as_bf16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+          if (GU) {
+            const f16x2 sv = e4m3x2_to_f16(sp[c][nb]);
+            b[nb] = __builtin_bit_cast(u32x4, dqh8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+          } else {
+            const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[c][nb], 1.0f, false);
+            b[nb] = __builtin_bit_cast(u32x4, dq8(wc[c][nb][wd], wd < 2 ? sv.x : sv.y));
+          }
+        }
+  #pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+  #pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (GU)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  as_f16x8(av_cur[mb]), as_f16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+            else
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(av_cur[mb]), as_bf16x8(b[nb]), acc[mb][nb], 0, 0, 0);
+          }
+        }
+        if (t < 7) {
+  #pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) av_cur[mb] = av_nxt[mb];
         }
       }
-      if (t < 7) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) av_cur[mb] = av_nxt[mb];
-      }
+      wait_vmcnt0();     // this wave's DMA of step s + 1 has landed
+      __syncthreads();   // ... and every wave's; stage st is free again
     }
-    wait_vmcnt0();     // this wave's DMA of step s + 1 has landed
-    __syncthreads();   // ... and every wave's; stage st is free again
-  }
 
-  // ---- epilogue ----
-  if (GU) {
-    const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
-    const int col = ti.nt * 32 * NW + 32 * wv + n32;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * mb + 8 * (i >> 2) + 4 * q + (i & 3);
-        if (r < ti.rows && sm.row_ok[r]) {
-          const float f = sm.row_fac[r];
-          const float g = acc[mb][0][i] * s2g * f, u = acc[mb][1][i] * s2u * f;
-          out[(size_t)(ti.p0 + r) * I + col] = f32_to_bf16_bits(silu_f32(g) * u);
-        }
-      }
-    }
-  } else {
-    const float s2d = scale2[3 * e + 2];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = ti.nt * WR + 32 * NW * nb + 32 * wv + n32;
-#pragma unroll
+    // ---- epilogue ----
+    // opaque copies (p0, and a zero added to the row-table offsets): the
+    // epilogue's addresses and row flags are rebuilt for each N tile instead
+    // of being hoisted out of the N-tile loop into registers
+    int p0 = ti.p0, z = 0;
+    asm volatile("" : "+s"(p0), "+s"(z));
+    if (GU) {
+      const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
+      const int col = j * 32 * NW + 32 * wv + n32;
+  #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+  #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 32 * mb + 8 * (i >> 2) + 4 * q + (i & 3);
-          if (r < ti.rows && sm.row_ok[r])
-            out[(size_t)(ti.p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][i] * s2d);
+          if (r < ti.rows && sm.row_ok[r + z]) {
+            const float f = sm.row_fac[r + z];
+            const float g = acc[mb][0][i] * s2g * f, u = acc[mb][1][i] * s2u * f;
+            out[(size_t)(p0 + r) * I + col] = f32_to_bf16_bits(silu_f32(g) * u);
+          }
+        }
+      }
+    } else {
+      const float s2d = scale2[3 * e + 2];
+  #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+  #pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int col = j * WR + 32 * NW * nb + 32 * wv + n32;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 32 * mb + 8 * (i >> 2) + 4 * q + (i & 3);
+            if (r < ti.rows && sm.row_ok[r + z])
+              out[(size_t)(p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][i] * s2d);
+          }
         }
       }
     }
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_prefill_gemm(
   __shared__ __align__(16) PfSmem<NW> sm;
   const int NT = GU ? I / (32 * NW) : H / (64 * NW);  // N tiles per group
   PfTile ti;
-  if (!pf_find_tile<NTHR>(offsets, G, NT, sm.base, sm.wsum, &ti)) return;
+  if (!pf_find_tile<NTHR>(offsets, G, 1, sm.base, sm.wsum, &ti)) return;  // item = row tile
   const int tid = threadIdx.x;
   for (int r = tid; r < kPM; r += NTHR) {
     int src = -1;
@@ -365,10 +377,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_prefill_gemm(
   }
   __syncthreads();
   switch ((ti.rows + 31) / 32) {  // uniform per block
-    case 1: pf_item<NW, GU, 1>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
-    case 2: pf_item<NW, GU, 2>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
-    case 3: pf_item<NW, GU, 3>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
-    default: pf_item<NW, GU, 4>(sm, ti, codes, scales, scale2, asrc, H, I, out); break;
+    case 1: pf_item<NW, GU, 1>(sm, ti, codes, scales, scale2, asrc, H, I, NT, out); break;
+    case 2: pf_item<NW, GU, 2>(sm, ti, codes, scales, scale2, asrc, H, I, NT, out); break;
+    case 3: pf_item<NW, GU, 3>(sm, ti, codes, scales, scale2, asrc, H, I, NT, out); break;
+    default: pf_item<NW, GU, 4>(sm, ti, codes, scales, scale2, asrc, H, I, NT, out); break;
   }
 }
 
@@ -389,20 +401,20 @@ hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const in
   const long mt_bound = S / kPM + G;
   const uint16_t* xa = (const uint16_t*)xh;
   if (I % 256 == 0) {
-    const dim3 g1((unsigned)(mt_bound * (I / 256)));
+    const dim3 g1((unsigned)mt_bound);
     MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<8, true>), g1, dim3(512), 0, s, W.gu_codes,
                W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
   } else {
-    const dim3 g1((unsigned)(mt_bound * (I / 128)));
+    const dim3 g1((unsigned)mt_bound);
     MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<4, true>), g1, dim3(256), 0, s, W.gu_codes,
                W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
   }
   if (H % 512 == 0) {
-    const dim3 g2((unsigned)(mt_bound * (H / 512)));
+    const dim3 g2((unsigned)mt_bound);
     MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<8, false>), g2, dim3(512), 0, s, W.dn_codes,
                W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
   } else {
-    const dim3 g2((unsigned)(mt_bound * (H / 256)));
+    const dim3 g2((unsigned)mt_bound);
     MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<4, false>), g2, dim3(256), 0, s, W.dn_codes,
                W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
   }
