@@ -206,7 +206,7 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
     ssrc[i] = scales + wrow(L >> 1) * srow + 4 * (L & 1);
   }
   int j = 0;  // N tile
-  auto dma_step = [&](int s, int st) {
+  auto dma_step = [&](int jt, int s, int st) {  // N tile jt, K step s, stage st
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       __builtin_amdgcn_global_load_lds(asrc_p[i] + 256 * s,
@@ -214,12 +214,12 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
                                        16, 0, 0);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc[i] + j * nt_codes + 64 * s,
+      __builtin_amdgcn_global_load_lds(wsrc[i] + jt * nt_codes + 64 * s,
                                        (__attribute__((address_space(3))) void*)&sm.Ws[st][1024 * (wv + NW * i)],
                                        16, 0, 0);
 #pragma unroll
     for (int i = 0; i < SI; ++i)
-      __builtin_amdgcn_global_load_lds(ssrc[i] + j * nt_scales + 8 * s,
+      __builtin_amdgcn_global_load_lds(ssrc[i] + jt * nt_scales + 8 * s,
                                        (__attribute__((address_space(3))) void*)&sm.Ss[st][256 * (wv + NW * i)],
                                        4, 0, 0);
   };
@@ -237,13 +237,16 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
       for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
 
     const int nsteps = KD / kPK;
-    dma_step(0, 0);
-    wait_vmcnt0();
-    __syncthreads();
+    if (j == 0) {  // later tiles had their first step prefetched by the previous tile
+      dma_step(0, 0, 0);
+      wait_vmcnt0();
+      __syncthreads();
+    }
     for (int s = 0; s < nsteps; ++s) {
-      const int st = s & 1;
+      const int st = (j * nsteps + s) & 1;  // stage parity runs on across N tiles
       // stage st ^ 1 was last read in step s - 1, which every wave has finished
-      if (s + 1 < nsteps) dma_step(s + 1, st ^ 1);
+      if (s + 1 < nsteps) dma_step(j, s + 1, st ^ 1);
+      else if (j + 1 < NT) dma_step(j + 1, 0, st ^ 1);  // the next tile's first step
       const uint8_t* A = sm.As[st];
       const uint8_t* Wt = sm.Ws[st];
       const uint8_t* St = sm.Ss[st];
@@ -308,7 +311,7 @@ __device__ __forceinline__ void pf_item(PfSmem<NW>& sm, const PfTile& ti,
           for (int mb = 0; mb < NMB; ++mb) av_cur[mb] = av_nxt[mb];
         }
       }
-      wait_vmcnt0();     // this wave's DMA of step s + 1 has landed
+      wait_vmcnt0();     // this wave's DMA of the next step has landed
       __syncthreads();   // ... and every wave's; stage st is free again
     }
 
