@@ -47,8 +47,8 @@ struct PfTile {
 // ones fill the end of the launch: class 0 holds the row tiles with 4 valid
 // 32-row blocks (every full tile, and a last tile of more than 96 rows),
 // classes 1, 2, 3 the last tiles with 3, 2, 1 valid blocks; within a class,
-// group by group, N tile by N tile, row tile by row tile.  The four per-group
-// counts are scanned at once as 16-bit fields of a 64-bit word.  All threads
+// group by group, row tile by row tile.  The four per-group counts are
+// scanned at once as fields of one 64-bit word.  All threads
 // must call it; false = no item.
 __device__ __forceinline__ unsigned long long pf_wave_incl_scan64(unsigned long long v, int lane) {
 #pragma unroll
@@ -59,8 +59,14 @@ __device__ __forceinline__ unsigned long long pf_wave_incl_scan64(unsigned long 
   return v;
 }
 
+// Field k of a packed count word: class 0 (full tiles, up to S/128 + G) in
+// bits [0, 31), classes 1..3 (at most one tile per group, G <= 1025) in 11
+// bits each from bit 31 on.
+__device__ __forceinline__ unsigned long long pf_unit(int k) {
+  return k == 0 ? 1ull : 1ull << (31 + 11 * (k - 1));
+}
 __device__ __forceinline__ int pf_field(unsigned long long v, int k) {
-  return (int)((v >> (16 * k)) & 0xFFFFull);
+  return k == 0 ? (int)(v & 0x7FFFFFFFull) : (int)((v >> (31 + 11 * (k - 1))) & 0x7FFull);
 }
 
 template <int NTHR>
@@ -73,7 +79,7 @@ __device__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT,
     const int rem = cnt % kPM;
     const int c0 = cnt / kPM + (rem > 96 ? 1 : 0);
     const int k = (rem > 0 && rem <= 96) ? 4 - (rem + 31) / 32 : 0;  // class of the last tile
-    base[g] = (unsigned long long)c0 | (k ? 1ull << (16 * k) : 0ull);
+    base[g] = (unsigned long long)c0 | (k ? pf_unit(k) : 0ull);
   }
   __syncthreads();
   const int per = (G + NTHR - 1) / NTHR;
