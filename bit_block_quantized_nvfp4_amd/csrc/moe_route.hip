@@ -1,14 +1,17 @@
 // Router top-K + softmax over the selected logits (A1).
 //
 // One wave64 per token.  Lane l holds logits l, l+64, l+128, ... in registers
-// (coalesced 256-byte loads).  K rounds of a wave arg-max pick the experts in
-// rank order (DPP inside rows of 16 lanes, readlane across rows); the arg-max
-// key is (logit descending, index ascending), NaN is
-// read as -inf, which is the tie rule of the page "handover briefs" (item A1
-// and the indexer-selection kernel spec: rank(b) counts the j with s_j > s_b or
-// s_j == s_b and j < b).  The weights are the softmax of the K selected logits
-// (equal to the renormalised full softmax), computed in fp32 with a fixed-order
-// butterfly sum.
+// (coalesced 256-byte loads) and sorts its own keys once, largest first (a
+// stable odd-even transposition sort, so equal keys stay in index order).
+// Each of the K rounds then takes one wave max over the 64 list heads (DPP
+// inside rows of 16 lanes, row broadcasts across rows); the lane holding it
+// pops its head.  When several heads hold the max, the lowest expert index
+// wins (a wave min over those heads).  The arg-max key is (logit descending,
+// index ascending), NaN is read as -inf, which is the tie rule of the page
+// "handover briefs" (item A1 and the indexer-selection kernel spec: rank(b)
+// counts the j with s_j > s_b or s_j == s_b and j < b).  The weights are the
+// softmax of the K selected logits (equal to the renormalised full softmax),
+// computed in fp32 with a fixed-order butterfly sum.
 #include <limits.h>
 #include <math.h>
 
@@ -32,18 +35,25 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Max / min over the 64 lanes, the same value in every lane: DPP xor-1, xor-2
-// (quad permutes), half-row and row mirrors inside each row of 16 lanes, then
-// readlane of lanes 0, 16, 32, 48.
+// Max over the 64 lanes, as a uniform value: DPP xor-1, xor-2 (quad
+// permutes), half-row and row mirrors leave each row's max in all its lanes;
+// row broadcasts of lane 15 (into rows 1, 3) and lane 31 (into rows 2, 3)
+// leave the wave's max in lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp<0xB1>(v));
   v = max(v, dpp<0x4E>(v));
   v = max(v, dpp<0x141>(v));
   v = max(v, dpp<0x140>(v));
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return max(a, b);
+  v = max(v, dpp_rows<0x142, 0xA>(v));
+  v = max(v, dpp_rows<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+// Min over the 64 lanes (the tie case only): quad and row steps as above,
+// then readlane of lanes 0, 16, 32, 48.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp<0xB1>(v));
   v = min(v, dpp<0x4E>(v));
@@ -63,7 +73,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
 
-  uint32_t key[MAXV];
+  uint32_t key[MAXV], jx[MAXV];  // key and slot j (expert lane + 64 j) of each entry
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int e = lane + 64 * j;
@@ -71,32 +81,47 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     if (e < E) z = row[e];
     // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
     key[j] = (e < E) ? logit_key((z != z) ? -INFINITY : z) : 0u;
+    jx[j] = (uint32_t)j;
+  }
+  // largest key first; a swap only on a strictly larger key keeps equal keys
+  // in ascending j, i.e. ascending expert index
+#pragma unroll
+  for (int pass = 0; pass < MAXV; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < MAXV; i += 2) {
+      const bool sw = key[i + 1] > key[i];
+      const uint32_t k0 = key[i], k1 = key[i + 1], j0 = jx[i], j1 = jx[i + 1];
+      key[i] = sw ? k1 : k0;
+      key[i + 1] = sw ? k0 : k1;
+      jx[i] = sw ? j1 : j0;
+      jx[i + 1] = sw ? j0 : j1;
+    }
   }
 
   float zsel = -INFINITY;
   int isel = 0;
   for (int k = 0; k < K; ++k) {
-    // best remaining key of this lane; indices ascend with j, so a strict '>'
-    // keeps the lower index among equal keys
-    uint32_t bk = 0u;
-    int bj = -1;
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j)
-      if (key[j] > bk) {
-        bk = key[j];
-        bj = j;
-      }
-    const uint32_t kmax = wave_max_u32(bk);
-    const uint32_t cand = (bj >= 0 && bk == kmax) ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu;
-    const int win = (int)wave_min_u32(cand);  // lowest expert index holding the max key
+    const uint32_t kmax = wave_max_u32(key[0]);
+    const bool has = key[0] == kmax;
+    const unsigned long long m = __ballot(has);
+    int win;  // expert index of the winner
+    if (__popcll(m) == 1) {
+      const int wl = __ffsll((long long)m) - 1;
+      win = wl + 64 * __builtin_amdgcn_readlane((int)jx[0], wl);
+    } else {
+      win = (int)wave_min_u32(has ? (uint32_t)lane + 64u * jx[0] : 0xFFFFFFFFu);
+    }
     if (lane == k) {
       zsel = key_logit(kmax);
       isel = win;
     }
-    if ((win & 63) == lane) {
+    if (lane == (win & 63)) {  // pop the head: the next largest becomes the head
 #pragma unroll
-      for (int j = 0; j < MAXV; ++j)
-        if (j == (win >> 6)) key[j] = 0u;  // taken: below every remaining key
+      for (int i = 0; i + 1 < MAXV; ++i) {
+        key[i] = key[i + 1];
+        jx[i] = jx[i + 1];
+      }
+      key[MAXV - 1] = 0u;
     }
   }
 
