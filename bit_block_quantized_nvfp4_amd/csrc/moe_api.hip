@@ -201,8 +201,6 @@ int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
     return fail(MOE_EINVAL, "moe_expert_ffn: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
   if (W->H < 256 || W->H > 4096 || W->H % 256 != 0 || W->I < 128 || W->I > 1024 || W->I % 128 != 0)
     return fail(MOE_EINVAL, "moe_expert_ffn: need H a multiple of 256 in [256, 4096] and I a multiple of 128 in [128, 1024] (H=%d I=%d)", W->H, W->I);
-  if ((long long)T * W->H * 2 > 0xFFFFFFFFll)
-    return fail(MOE_EINVAL, "moe_expert_ffn: need T * H * 2 < 2^32 (T=%d H=%d)", T, W->H);
   const size_t need = moe::ffn_workspace_bytes(T, K, W->H, W->I, W->has_shared, act_mode);
   if (!ws || ws_bytes < need)
     return fail(MOE_EWORKSPACE, "moe_expert_ffn: workspace of %zu bytes needed, %zu given", need, ws_bytes);

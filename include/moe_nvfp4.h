@@ -36,9 +36,8 @@
  *    inputs give bitwise identical outputs.
  *
  * Limits: T >= 1, 1 <= K <= 32, K <= E <= 1024; for the expert FFN H is a
- * multiple of 256 in [256, 4096], I a multiple of 128 in [128, 1024] and
- * T * H * 2 < 2^32 (the activation rows are addressed with 32-bit offsets);
- * for the combine H is a multiple of 8.  The library builds for gfx950
+ * multiple of 256 in [256, 4096] and I a multiple of 128 in [128, 1024]; for
+ * the combine H is a multiple of 8.  The library builds for gfx950
  * only; moe_init() refuses any other device.
  */
 #ifndef MOE_NVFP4_H
