@@ -46,6 +46,35 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// DPP move of v from the lane that control CTRL names (all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// The same, written only in the rows of mask ROWS (other lanes keep v).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+// Max over the 64 lanes, as a uniform value, without LDS: DPP xor-1, xor-2
+// (quad permutes), half-row and row mirrors leave each row's max in all its
+// lanes; row broadcasts of lane 15 (into rows 1, 3) and lane 31 (into rows
+// 2, 3) leave the wave's max in lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  v = max(v, dpp_rows<0x142, 0xA>(v));
+  v = max(v, dpp_rows<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Max over the lanes of a float that is >= 0 and not NaN in every lane (the
+// bit patterns of such floats order like their values).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  return __uint_as_float(wave_max_u32(__float_as_uint(v)));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll

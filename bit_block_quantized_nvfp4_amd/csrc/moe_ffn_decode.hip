@@ -264,25 +264,47 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // (5) activation rows -> f16 in place (LDS only; the barrier that follows
   // waits for LDS traffic, not for the code loads in flight)
-  // Two passes over the row in LDS (absmax, then convert), one chunk in
-  // registers at a time: the code words in flight keep their registers.
-  for (int r = wv; r < TR; r += WPB) {
-    float amax = 0.f;
-    for (int ch = lane; ch < CPR; ch += 64) {
-      const u32x4 v = *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR));
+  // Two passes over each row in LDS (absmax, then convert), one chunk in
+  // registers at a time: the code words in flight keep their registers.  A
+  // wave's rows go through each phase together, and the absmax reduction is
+  // DPP-only (no LDS round trips).
+  constexpr int RPW = (TR + WPB - 1) / WPB;  // rows per wave
+  constexpr int NCL = (CPR + 63) / 64;        // chunks of a row per lane
+  float amax[RPW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+  for (int ri = 0; ri < RPW; ++ri) {
+    const int r = wv + WPB * ri;
+    amax[ri] = 0.f;
+    if (r < TR) {
+      u32x4 v[NCL];  // all of the lane's chunks of the row in flight at once
+#pragma unroll
+      for (int k = 0; k < NCL; ++k) {
+        const int ch = lane + 64 * k;
+        v[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                        : u32x4{0u, 0u, 0u, 0u};
       }
+#pragma unroll
+      for (int k = 0; k < NCL; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          amax[ri] = fmaxf(amax[ri], fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
+          amax[ri] = fmaxf(amax[ri], fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
+        }
     }
-    amax = wave_max(amax);
+  }
+  // fmaxf drops NaN, so every lane's value is >= 0 and not NaN
+#pragma unroll
+  for (int ri = 0; ri < RPW; ++ri) amax[ri] = wave_max_nonneg(amax[ri]);
+#pragma unroll
+  for (int ri = 0; ri < RPW; ++ri) {
+    const int r = wv + WPB * ri;
+    if (r >= TR) break;  // uniform per wave
     float mul, rf;
     if (FP8) {
-      rf = amax > 0.f ? amax / 448.0f : 1.0f;
-      mul = amax > 0.f ? 448.0f / amax : 1.0f;
+      rf = amax[ri] > 0.f ? amax[ri] / 448.0f : 1.0f;
+      mul = amax[ri] > 0.f ? 448.0f / amax[ri] : 1.0f;
     } else {
-      const int sh = f16_row_shift(amax);
+      const int sh = f16_row_shift(amax[ri]);
       mul = ldexpf(1.0f, sh);
       rf = ldexpf(1.0f, -sh);
     }
@@ -291,9 +313,19 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       fac[r] = rf;
       if (wr) xs[r] = rf;
     }
-    for (int ch = lane; ch < CPR; ch += 64) {
+    u32x4 vr[NCL];
+#pragma unroll
+    for (int k = 0; k < NCL; ++k) {
+      const int ch = lane + 64 * k;
+      vr[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < NCL; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch >= CPR) break;
       uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
-      const u32x4 v = *(const u32x4*)pch;
+      const u32x4 v = vr[k];
       u32x4 o;
       if (FP8) {
         u32x2 code;

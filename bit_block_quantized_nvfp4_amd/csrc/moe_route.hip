@@ -30,28 +30,8 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Max over the 64 lanes, as a uniform value: DPP xor-1, xor-2 (quad
-// permutes), half-row and row mirrors leave each row's max in all its lanes;
-// row broadcasts of lane 15 (into rows 1, 3) and lane 31 (into rows 2, 3)
-// leave the wave's max in lane 63.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp<0xB1>(v));
-  v = max(v, dpp<0x4E>(v));
-  v = max(v, dpp<0x141>(v));
-  v = max(v, dpp<0x140>(v));
-  v = max(v, dpp_rows<0x142, 0xA>(v));
-  v = max(v, dpp_rows<0x143, 0xC>(v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
+// wave_max_u32 (moe_device.hpp) gives the max; the min below is used only on
+// an exact tie.
 // Min over the 64 lanes (the tie case only): quad and row steps as above,
 // then readlane of lanes 0, 16, 32, 48.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
