@@ -209,14 +209,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
   const int nbk = I / 16 / WPB;
   const int a = blockIdx.x / nbk, pb = (blockIdx.x % nbk) * WPB + wv;
-  // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
-  const int nact = groups[0], e = groups[1 + a];
-  asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
-  if (a >= nact) return;      // uniform per block, before any load is in flight
-  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
-  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
 
-  // (1) activation rows (bf16) and the unit's scale runs -> LDS
+  // (1) activation rows (bf16) -> LDS, first of all: they do not depend on
+  // the group, and issued ahead of every code load on the CU they land early,
+  // so their conversion stays off the critical path
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int base = 64 * (wv + WPB * i), L = base + lane;
@@ -225,6 +221,17 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       dma16(x + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
     }
   }
+  // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
+  const int nact = groups[0], e = groups[1 + a];
+  asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
+  if (a >= nact) {            // uniform per block: nothing to do, but the DMA into
+    wait_vmcnt<0>();          // this block's LDS must land before the block ends
+    return;
+  }
+  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
+  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
+
+  // the unit's scale runs -> LDS
   const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
   {
     const uint8_t* sg = gu_scales + grow * (H / 16);
@@ -256,10 +263,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
   const int slot_l = sorted_slot[p0 + (lane < n ? lane : n - 1)];
 
-  // (4) this wave's DMA is complete once at most the 2*NCH youngest loads are
-  // outstanding; the barrier then covers the whole block.  The code chunks
-  // are waited for one by one as the MFMAs reach them.
-  wait_vmcnt<2 * NCH>();
+  // (4) this wave's activation DMA is complete once at most the scale DMA,
+  // the code loads and the slot load behind it are outstanding; the barrier
+  // then covers the whole block.
+  constexpr int kScaleDma = 2 * (SRUN % 1024 == 0 ? SRUN / 1024 : SRUN / 256);
+  wait_vmcnt<kScaleDma + 2 * NCH + 1>();
   __builtin_amdgcn_s_barrier();
 
   // (5) activation rows -> f16 in place (LDS only; the barrier that follows
@@ -355,6 +363,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       *(u32x4*)pch = o;
     }
   }
+  // the scale runs have landed once only the code loads (and the slot load)
+  // are outstanding; the code chunks are waited for one by one as the MFMAs
+  // reach them.  LDS traffic done, then the barrier publishes the rows.
+  wait_vmcnt<2 * NCH>();
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   float ums[8];
