@@ -131,12 +131,12 @@ __global__ __launch_bounds__(256) void k_dec_xprep(const uint16_t* __restrict__ 
 // contiguous runs (16 gate rows, 16 up rows, H/16 bytes each) and go to LDS
 // by DMA; each chunk's scale pair is read from there.
 //
-// Load order (all issued before the first wait): the group lookup, then the
-// activation rows and the scale runs straight into LDS (global->LDS DMA, no
-// registers), then every code word of the unit, then the epilogue's
-// metadata.  The activation rows are unpadded with the 16-byte chunk index
-// XOR-swizzled by (row & 15), so the A-operand reads of 16 rows at one chunk
-// hit 16 distinct bank groups.
+// Load order (all issued before the first wait): the activation rows straight
+// into LDS (global->LDS DMA, no registers; they do not depend on the group),
+// the group lookup, the unit's scale runs into LDS, every code word of the
+// unit, then the epilogue's metadata.  The activation rows are unpadded with
+// the 16-byte chunk index XOR-swizzled by (row & 15), so the A-operand reads
+// of 16 rows at one chunk hit 16 distinct bank groups.
 
 // Copy BYTES contiguous bytes (a multiple of 256) from global memory to LDS
 // with one wave: 16 bytes per lane when BYTES is a multiple of 1 KB, else 4.

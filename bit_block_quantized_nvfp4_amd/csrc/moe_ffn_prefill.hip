@@ -18,13 +18,14 @@
 // skipped).  Every weight byte is dequantised exactly once per row tile; the
 // A tile is shared by all waves.
 //
-// K runs in steps of 128.  Each step's A tile (128 rows x 256 B), weight
-// codes (64*NW rows x 64 B) and block scales (64*NW rows x 8 B) are loaded by
-// all threads with row-contiguous 16-byte accesses (every 64 B of a weight row
-// by 4 adjacent lanes) into registers while the previous step computes, then
-// written to the other half of a double-buffered LDS stage; one barrier per
-// step.  LDS rows are XOR-swizzled in 16-byte chunks so that the MFMA operand
-// reads of 16 consecutive rows at one chunk hit distinct banks.
+// K runs in steps of 128.  Each step's A tile (the valid 32-row blocks of 128
+// rows x 256 B), weight codes (64*NW rows x 64 B) and block scales (64*NW
+// rows x 8 B) go from global memory straight into the other half of a
+// double-buffered LDS stage by global->LDS DMA, issued one step ahead while
+// the current step computes (every 64 B of a weight row by 4 adjacent lanes,
+// 16 bytes each); one wait and one barrier per step.  LDS rows are
+// XOR-swizzled in 16-byte chunks so that the MFMA operand reads of 16
+// consecutive rows at one chunk hit distinct banks.
 //
 // Lane (n = l%32, q = l/32) of sub-step (c, wd), c in {0,1}, wd in 0..3: MFMA
 // k index 8q + i is element 64c + 32q + 8wd + i of the step on both operands
