@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -69,19 +71,47 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_rows<0x143, 0xC>(v));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+// Sum over the 64 lanes, as a uniform value, in a fixed order and without
+// LDS: the same DPP steps as wave_max_u32 with adds.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  auto mv = [](float x, auto ctrl, auto rows) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      decltype(rows)::value, 0xF, false));
+  };
+  using C1 = std::integral_constant<int, 0xB1>;
+  using C2 = std::integral_constant<int, 0x4E>;
+  using C3 = std::integral_constant<int, 0x141>;
+  using C4 = std::integral_constant<int, 0x140>;
+  using C5 = std::integral_constant<int, 0x142>;
+  using C6 = std::integral_constant<int, 0x143>;
+  using RA = std::integral_constant<int, 0xF>;
+  v += mv(v, C1{}, RA{});
+  v += mv(v, C2{}, RA{});
+  v += mv(v, C3{}, RA{});
+  v += mv(v, C4{}, RA{});
+  v += mv(v, C5{}, std::integral_constant<int, 0xA>{});
+  v += mv(v, C6{}, std::integral_constant<int, 0xC>{});
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 // Max over the lanes of a float that is >= 0 and not NaN in every lane (the
 // bit patterns of such floats order like their values).
 __device__ __forceinline__ float wave_max_nonneg(float v) {
   return __uint_as_float(wave_max_u32(__float_as_uint(v)));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, without LDS: row shifts
+// by 1, 2, 4, 8 (a lane with no source adds 0) give each row of 16 lanes its
+// own prefix sums; row broadcasts of lane 15 (into rows 1, 3) and lane 31
+// (into rows 2, 3) add the totals of the rows before.  lane is unused (kept
+// for the callers' symmetry with the 64-bit scan).
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  (void)lane;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 

@@ -51,12 +51,24 @@ struct PfTile {
 // group by group, row tile by row tile.  The four per-group counts are
 // scanned at once as fields of one 64-bit word.  All threads
 // must call it; false = no item.
+// The 64-bit word moved by one DPP control (both halves; 0 where the control
+// has no source lane or the row is masked off).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long pf_dpp64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// Inclusive prefix sum of a 64-bit word over the 64 lanes, without LDS: row
+// shifts by 1, 2, 4, 8, then row broadcasts of lanes 15 and 31.
 __device__ __forceinline__ unsigned long long pf_wave_incl_scan64(unsigned long long v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const unsigned long long o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  (void)lane;
+  v += pf_dpp64<0x111, 0xF>(v);  // row_shr:1
+  v += pf_dpp64<0x112, 0xF>(v);  // row_shr:2
+  v += pf_dpp64<0x114, 0xF>(v);  // row_shr:4
+  v += pf_dpp64<0x118, 0xF>(v);  // row_shr:8
+  v += pf_dpp64<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += pf_dpp64<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 

@@ -54,15 +54,15 @@ __device__ int block_exclusive_scan(int* a, int n, int* wsum) {
   return total;
 }
 
-// Ranks one chunk of up to 256 slots starting at c0 and scatters them.
-// run[e] holds the next free position of group e and is advanced here.
-__device__ void scatter_chunk(const int32_t* __restrict__ ids, int TK, int E, int c0,
+// Ranks one chunk of up to 256 slots starting at c0 and scatters them; e is
+// the expert id of this thread's slot c0 + tid (ignored past TK).  run[e]
+// holds the next free position of group e and is advanced here.
+__device__ void scatter_chunk(int e, int TK, int E, int c0,
                               unsigned long long (*masks)[kMaxE], int* run,
                               int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s = c0 + tid;
   const bool in = s < TK;
-  const int e = in ? ids[s] : -1;
   const bool ok = in && e >= 0 && e < E;
   const unsigned long long bit = 1ull << lane;
   if (ok) atomicOr(&masks[wv][e], bit);
@@ -129,10 +129,14 @@ __global__ __launch_bounds__(kBlock) void k_permute_small(
   __shared__ int wsum[kBlock / 64];
   const int tid = threadIdx.x;
   const int TK = T * K, G = E + has_shared;
+  // this thread's slot of the first chunk, loaded once (the whole input when
+  // T*K <= 256), in flight during the LDS set-up
+  const int id0 = tid < TK ? ids[tid] : -1;
   for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
   for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : 0;
   __syncthreads();
-  for (int s = tid; s < TK; s += kBlock) {
+  if (id0 >= 0 && id0 < E) atomicAdd(&run[id0], 1);
+  for (int s = tid + kBlock; s < TK; s += kBlock) {
     const int e = ids[s];
     if (e >= 0 && e < E) atomicAdd(&run[e], 1);
   }
@@ -144,7 +148,11 @@ __global__ __launch_bounds__(kBlock) void k_permute_small(
   for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
   if (tid == 0) offsets[G] = total;
   const int off_shared = has_shared ? run[E] : 0;  // scatter_chunk only moves run[e < E]
-  for (int c0 = 0; c0 < TK; c0 += kChunk) scatter_chunk(ids, TK, E, c0, masks, run, sorted_slot, slot_pos);
+  static_assert(kChunk == kBlock, "one slot per thread and chunk");
+  for (int c0 = 0; c0 < TK; c0 += kChunk) {
+    const int s = c0 + tid;
+    scatter_chunk(c0 == 0 ? id0 : (s < TK ? ids[s] : -1), TK, E, c0, masks, run, sorted_slot, slot_pos);
+  }
   if (has_shared) write_shared_group(T, TK, off_shared, sorted_slot, slot_pos, tid, kBlock);
 }
 
@@ -214,7 +222,10 @@ __global__ __launch_bounds__(kBlock) void k_permute_scatter(
   for (int e = tid; e < E; e += kBlock) run[e] += cnt[(size_t)e * ntiles + tile];
   __syncthreads();
   const int s0 = tile * kTileSlots, s1 = min(s0 + kTileSlots, TK);
-  for (int c0 = s0; c0 < s1; c0 += kChunk) scatter_chunk(ids, s1, E, c0, masks, run, sorted_slot, slot_pos);
+  for (int c0 = s0; c0 < s1; c0 += kChunk) {
+    const int s = c0 + threadIdx.x;
+    scatter_chunk(s < s1 ? ids[s] : -1, s1, E, c0, masks, run, sorted_slot, slot_pos);
+  }
   if (has_shared)
     write_shared_group(T, TK, off_shared, sorted_slot, slot_pos, tile * kBlock + tid, ntiles * kBlock);
 }

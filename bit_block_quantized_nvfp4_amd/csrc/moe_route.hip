@@ -11,7 +11,7 @@
 // "handover briefs" (item A1 and the indexer-selection kernel spec: rank(b)
 // counts the j with s_j > s_b or s_j == s_b and j < b).  The weights are the
 // softmax of the K selected logits (equal to the renormalised full softmax),
-// computed in fp32 with a fixed-order butterfly sum.
+// computed in fp32 with a fixed-order DPP sum.
 #include <limits.h>
 #include <math.h>
 
@@ -105,10 +105,10 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     }
   }
 
-  const float z0 = __shfl(zsel, 0, 64);
+  const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zsel), 0));
   float ex = 0.f;
   if (lane < K) ex = expf(zsel == z0 ? 0.f : zsel - z0);
-  const float sum = wave_sum(ex);
+  const float sum = wave_sum_dpp(ex);
   if (lane < K) {
     ids[(size_t)t * K + lane] = isel;
     w[(size_t)t * K + lane] = ex / sum;
