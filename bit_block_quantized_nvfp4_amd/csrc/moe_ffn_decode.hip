@@ -25,7 +25,9 @@
 //
 // k_dec_down: unit = (active group, 64 output rows as 4 MFMA blocks of 16);
 // A = the group's h rows (bf16, by sorted position), up to 16 per pass, in
-// LDS; bf16 MFMA 16x16x32.
+// LDS, turned into f16 in place with a per-row power-of-two shift (undone in
+// the epilogue); f16 MFMA 16x16x32 against weights dequantised to f16 at one
+// instruction per element.
 //
 // Lane (r = l%16, q = l/16) of either kernel: B column r = weight row, A row r
 // = token row (or group row).  The lane's 16-byte code chunk c is bytes
@@ -419,7 +421,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 // (the permutation only places valid ones), so the rows are read without a
 // slot lookup; rows of a pass past the group's end repeat its last row and
 // are not stored.
-// Dynamic LDS: [16][I] bf16 h rows, then per wave the scale run (64 x I/16 B).
+// Dynamic LDS: [16][I] h rows (bf16 as loaded, f16 after the conversion),
+// then per wave the scale run (64 x I/16 B), then the 16 rows' epilogue
+// factors (f32).
 template <int NCH, int WPB>   // NCH = I / 128
 __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
@@ -471,35 +475,77 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   const float s2d = scale2[3 * e + 2];
   const uint8_t* hrow = (const uint8_t*)hl;
   const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  float* hfac = (float*)((uint8_t*)hl + (size_t)16 * I * 2 + (size_t)WPB * SRUN);  // [16]
+  // The staged bf16 h rows of a pass -> f16 in place, each row times the
+  // power of two that brings its absmax into [2^14, 2^15) (the rule of the
+  // activation rows in gate_up), undone in the epilogue; rows past the
+  // group's end are left as they are (their outputs are never stored).
+  constexpr int NCLD = (16 * NCH + 63) / 64;  // 16-byte chunks of a row per lane
+  auto convert_h = [&](int r0) {
+    const int nv = n - r0 < 16 ? n - r0 : 16;  // valid rows of the pass
+    for (int r = wv; r < nv; r += WPB) {
+      u32x4 v[NCLD];
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k) {
+        const int ch = lane + 64 * k;
+        v[k] = ch < cpr ? *(const u32x4*)(hrow + swz_off(r, ch, cpr)) : u32x4{0u, 0u, 0u, 0u};
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][jj] & 0xFFFFu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][jj] >> 16)));
+        }
+      amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
+      const int sh = f16_row_shift(amax);
+      const float mul = ldexpf(1.0f, sh);
+      if (lane == 0) hfac[r] = ldexpf(1.0f, -sh);
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch >= cpr) break;
+        u32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          o[jj] = pack_f16x2(bf16_bits_to_f32(v[k][jj] & 0xFFFFu) * mul,
+                             bf16_bits_to_f32(v[k][jj] >> 16) * mul);
+        *(u32x4*)((uint8_t*)hl + swz_off(r, ch, cpr)) = o;
+      }
+    }
+  };
   auto compute = [&](int r0) {
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      f32x2 sc[4];
+      f16x2 sc[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        sc[nb] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(
-            *(const uint16_t*)(srow + nb * 16 * (8 * NCH) + 8 * c), 1.0f, false);
+        sc[nb] = e4m3x2_to_f16(*(const uint16_t*)(srow + nb * 16 * (8 * NCH) + 8 * c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4*)(hrow + swz_off(r16, 16 * c + 4 * q + j, cpr)));
+        const f16x8 av = __builtin_bit_cast(f16x8, *(const u32x4*)(hrow + swz_off(r16, 16 * c + 4 * q + j, cpr)));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, dq8(w[nb][c][j], j < 2 ? sc[nb].x : sc[nb].y), acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w[nb][c][j], j < 2 ? sc[nb].x : sc[nb].y), acc[nb], 0, 0, 0);
       }
       // keep each chunk's dequantised operands next to their MFMAs (bounds
       // the registers in flight)
       __builtin_amdgcn_sched_barrier(0);
     }
+    float rf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rf[i] = hfac[4 * q + i];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int col = rb * 64 + nb * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int mm = 4 * q + i;
-        if (r0 + mm < n) y[(size_t)(p0 + r0 + mm) * H + col] = f32_to_bf16_bits(acc[nb][i] * s2d);
+        if (r0 + mm < n) y[(size_t)(p0 + r0 + mm) * H + col] = f32_to_bf16_bits(acc[nb][i] * rf[i] * s2d);
       }
     }
   };
@@ -507,10 +553,15 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   // outstanding; the barrier covers the block
   wait_vmcnt<4 * (NCH - NH)>();
   __builtin_amdgcn_s_barrier();
+  convert_h(0);
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
   compute(0);
   for (int r0 = 16; r0 < n; r0 += 16) {  // only when ids repeat (> 16 rows)
-    __syncthreads();  // previous pass done reading hl
+    __syncthreads();  // previous pass done reading hl and hfac
     stage(r0);
+    __syncthreads();
+    convert_h(r0);
     __syncthreads();
     // the code words count as redefined on every pass, so the dequantised
     // operands (4x the registers of the codes) are not hoisted out of the loop
@@ -635,7 +686,7 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   else return hipErrorInvalidValue;
 #undef MOE_DEC_GU
   const dim3 g2((unsigned)(dn_units / wpb_d)), b2(64 * wpb_d);
-  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)wpb_d * 64 * (I / 16);
+  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)wpb_d * 64 * (I / 16) + 16 * sizeof(float);
   const int ncd = I / 128;
 #define MOE_DEC_DN(NCH)                                                                            \
   do {                                                                                             \
