@@ -35,18 +35,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
 }
 
-// ---- wave-level reductions (xor butterfly: every lane ends with the same,
-// order-fixed result) ----
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
+// ---- wave-level reductions and scans on DPP (no LDS round trips; every
+// result is order-fixed and uniform or per lane as stated) ----
 
 // DPP move of v from the lane that control CTRL names (all rows and banks).
 template <int CTRL>

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_dec_xprep(const uint16_t* __restrict__ 
       }
     }
   }
-  amax = wave_max(amax);
+  amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
