@@ -274,19 +274,15 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // (5) activation rows -> f16 in place (LDS only; the barrier that follows
   // waits for LDS traffic, not for the code loads in flight)
-  // Two passes over each row in LDS (absmax, then convert), one chunk in
-  // registers at a time: the code words in flight keep their registers.  A
-  // wave's rows go through each phase together, and the absmax reduction is
-  // DPP-only (no LDS round trips).
-  constexpr int RPW = (TR + WPB - 1) / WPB;  // rows per wave
-  constexpr int NCL = (CPR + 63) / 64;        // chunks of a row per lane
-  float amax[RPW];
-#pragma unroll
-  for (int ri = 0; ri < RPW; ++ri) {
-    const int r = wv + WPB * ri;
-    amax[ri] = 0.f;
-    if (r < TR) {
-      u32x4 v[NCL];  // all of the lane's chunks of the row in flight at once
+  // Two passes over each row in LDS (absmax, then convert), one row at a
+  // time so that the code words in flight keep their registers; each pass
+  // issues all of the lane's chunks of the row at once, and the absmax
+  // reduction is DPP-only (no LDS round trips).
+  constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
+  for (int r = wv; r < TR; r += WPB) {
+    float amax = 0.f;
+    {
+      u32x4 v[NCL];
 #pragma unroll
       for (int k = 0; k < NCL; ++k) {
         const int ch = lane + 64 * k;
@@ -297,24 +293,17 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int k = 0; k < NCL; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          amax[ri] = fmaxf(amax[ri], fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
-          amax[ri] = fmaxf(amax[ri], fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
         }
     }
-  }
-  // fmaxf drops NaN, so every lane's value is >= 0 and not NaN
-#pragma unroll
-  for (int ri = 0; ri < RPW; ++ri) amax[ri] = wave_max_nonneg(amax[ri]);
-#pragma unroll
-  for (int ri = 0; ri < RPW; ++ri) {
-    const int r = wv + WPB * ri;
-    if (r >= TR) break;  // uniform per wave
+    amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
     float mul, rf;
     if (FP8) {
-      rf = amax[ri] > 0.f ? amax[ri] / 448.0f : 1.0f;
-      mul = amax[ri] > 0.f ? 448.0f / amax[ri] : 1.0f;
+      rf = amax > 0.f ? amax / 448.0f : 1.0f;
+      mul = amax > 0.f ? 448.0f / amax : 1.0f;
     } else {
-      const int sh = f16_row_shift(amax[ri]);
+      const int sh = f16_row_shift(amax);
       mul = ldexpf(1.0f, sh);
       rf = ldexpf(1.0f, -sh);
     }
@@ -664,12 +653,15 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
-  // Waves (units) per block: 4 when there are enough units to fill the
-  // chip, else 1 so that small T still spreads over many CUs.
+  // Waves (units) per block: 4 (one staged copy of the activation or h rows
+  // per 4 units) once the units are plentiful, else 1 so that small T still
+  // spreads over many CUs.  Measured crossovers (H=2048, I=512, 256 CUs):
+  // gate_up gains from 4 from about 2 units per CU on (T=3: 15.8 vs 17.8 us,
+  // T=6: 22.3 vs 37 us), down from about 1.
   const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
   const long cus = num_cus();
-  const int wpb_g = gu_units >= 8 * cus ? 4 : 1;
-  const int wpb_d = dn_units >= 8 * cus ? 4 : 1;
+  const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
+  const int wpb_d = dn_units >= cus ? 4 : 1;
   const dim3 g1((unsigned)(gu_units / wpb_g));
   const int nch = H / 128;
 #define MOE_DEC_GU(NCH)                                                                          \
