@@ -272,8 +272,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   wait_vmcnt<kScaleDma + 2 * NCH + 1>();
   __builtin_amdgcn_s_barrier();
 
-  // (5) activation rows -> f16 in place (LDS only; the barrier that follows
-  // waits for LDS traffic, not for the code loads in flight)
+  // (5) activation rows -> f16 in place (LDS only; the wait and barrier that
+  // follow cover the scale runs and the LDS traffic, not the code loads in
+  // flight)
   // Two passes over each row in LDS (absmax, then convert), one row at a
   // time so that the code words in flight keep their registers; each pass
   // issues all of the lane's chunks of the row at once, and the absmax
