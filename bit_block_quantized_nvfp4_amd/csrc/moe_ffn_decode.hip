@@ -369,6 +369,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   const int xr = r16 < T ? r16 : T - 1;
   const uint8_t* xrow = (const uint8_t*)xl;
   const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  // the swizzle touches only the low 4 bits of the chunk index, so the
+  // operand of sub-MFMA (c, j) sits at aoff[j] + 256 c (an immediate offset)
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = swz_off(xr, 4 * q + j, CPR);
   f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
     const f16x2 suv = e4m3x2_to_f16(*(const uint16_t*)(srow + SRUN + 8 * c));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f16x8 av = *(const f16x8*)(xrow + swz_off(xr, 16 * c + 4 * q + j, CPR));
+      const f16x8 av = *(const f16x8*)(xrow + aoff[j] + 256 * c);
       dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wg[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
       du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wu[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
     }
@@ -465,6 +470,11 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   const float s2d = scale2[3 * e + 2];
   const uint8_t* hrow = (const uint8_t*)hl;
   const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  // A operand of sub-MFMA (c, j) at haoff[j] + 256 c (the swizzle touches only
+  // the low 4 bits of the chunk index)
+  int haoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) haoff[j] = swz_off(r16, 4 * q + j, cpr);
   float* hfac = (float*)((uint8_t*)hl + (size_t)16 * I * 2 + (size_t)WPB * SRUN);  // [16]
   // The staged bf16 h rows of a pass -> f16 in place, each row times the
   // power of two that brings its absmax into [2^14, 2^15) (the rule of the
@@ -517,7 +527,7 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
         sc[nb] = e4m3x2_to_f16(*(const uint16_t*)(srow + nb * 16 * (8 * NCH) + 8 * c));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f16x8 av = __builtin_bit_cast(f16x8, *(const u32x4*)(hrow + swz_off(r16, 16 * c + 4 * q + j, cpr)));
+        const f16x8 av = __builtin_bit_cast(f16x8, *(const u32x4*)(hrow + haoff[j] + 256 * c));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w[nb][c][j], j < 2 ? sc[nb].x : sc[nb].y), acc[nb], 0, 0, 0);
