@@ -79,6 +79,7 @@ def test_decode_layer_full_size(moe, T):
     dict(T=700, H=256, E=4, K=2, I=128, has_shared=True),        # several 128-row tiles per expert
     dict(T=9, H=512, E=16, K=4, I=256, has_shared=False),        # just above the decode switch
     dict(T=64, H=1024, E=512, K=10, I=384, has_shared=True),     # many empty experts, I % 256 != 0
+    dict(T=40, H=4096, E=8, K=2, I=1024, has_shared=True),       # largest H and I: 32 K steps, 4 + 8 N tiles
 ])
 def test_grouped_path_medium(moe, cfg):
     wl = make_workload("m", seed=3, **cfg)
@@ -122,6 +123,7 @@ def test_fp8_zero_rows(moe, T):
     dict(T=8, H=1024, E=16, K=8, I=128, has_shared=False),    # decode, one down chunk
     dict(T=2, H=4096, E=8, K=2, I=128, has_shared=True),      # T <= 8 with no decode variant: grouped path
     dict(T=5, H=1024, E=16, K=3, I=384, has_shared=True),     # I / 128 = 3: grouped path at T <= 8
+    dict(T=8, H=2048, E=16, K=4, I=1024, has_shared=True),    # decode at its largest H and I
 ])
 def test_small_T_shapes(moe, cfg):
     _full_check(moe, make_workload("q", seed=9, **cfg), tag=f"small T {cfg}")
