@@ -223,14 +223,100 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       dma16(x + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
     }
   }
+  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
+  // Activation rows -> f16 MFMA operand in LDS, in place (the rule of
+  // k_dec_xprep, bit for bit): wave wv converts rows wv, wv + WPB, ...; the
+  // row's epilogue factor goes to fac[]; with FP8, block 0 also writes the
+  // row codes and scales to xq / xs.
+  auto convert_rows = [&]() {
+    constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
+    for (int r = wv; r < TR; r += WPB) {
+      float amax = 0.f;
+      {
+        u32x4 v[NCL];
+#pragma unroll
+        for (int k = 0; k < NCL; ++k) {
+          const int ch = lane + 64 * k;
+          v[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < NCL; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
+            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
+          }
+      }
+      amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
+      float mul, rf;
+      if (FP8) {
+        rf = amax > 0.f ? amax / 448.0f : 1.0f;
+        mul = amax > 0.f ? 448.0f / amax : 1.0f;
+      } else {
+        const int sh = f16_row_shift(amax);
+        mul = ldexpf(1.0f, sh);
+        rf = ldexpf(1.0f, -sh);
+      }
+      const bool wr = FP8 && blockIdx.x == 0 && r < T;
+      if (lane == 0) {
+        fac[r] = rf;
+        if (wr) xs[r] = rf;
+      }
+      u32x4 vr[NCL];
+#pragma unroll
+      for (int k = 0; k < NCL; ++k) {
+        const int ch = lane + 64 * k;
+        vr[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                         : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < NCL; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch >= CPR) break;
+        uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
+        const u32x4 v = vr[k];
+        u32x4 o;
+        if (FP8) {
+          u32x2 code;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float f0 = bf16_bits_to_f32(v[2 * j] & 0xFFFFu) * mul;
+            float f1 = bf16_bits_to_f32(v[2 * j] >> 16) * mul;
+            float f2 = bf16_bits_to_f32(v[2 * j + 1] & 0xFFFFu) * mul;
+            float f3 = bf16_bits_to_f32(v[2 * j + 1] >> 16) * mul;
+            f0 = fminf(fmaxf(f0, -448.f), 448.f);
+            f1 = fminf(fmaxf(f1, -448.f), 448.f);
+            f2 = fminf(fmaxf(f2, -448.f), 448.f);
+            f3 = fminf(fmaxf(f3, -448.f), 448.f);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
+            code[j] = (uint32_t)w;
+          }
+          if (wr) *(u32x2*)(xq + (size_t)r * H + 8 * ch) = code;
+          const u32x2 lo = fp8x4_to_f16(code.x), hi = fp8x4_to_f16(code.y);
+          o = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xFFFFu) * mul,
+                              bf16_bits_to_f32(v[j] >> 16) * mul);
+        }
+        *(u32x4*)pch = o;
+      }
+    }
+  };
   // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
   if (a >= nact) {            // uniform per block: nothing to do, but the DMA into
     wait_vmcnt<0>();          // this block's LDS must land before the block ends
+    if (FP8 && blockIdx.x == 0) {  // the row codes and scales are outputs of the call
+      __builtin_amdgcn_s_barrier();  // even when no group is active
+      convert_rows();
+    }
     return;
   }
-  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
   uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
 
   // the unit's scale runs -> LDS
@@ -279,82 +365,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // time so that the code words in flight keep their registers; each pass
   // issues all of the lane's chunks of the row at once, and the absmax
   // reduction is DPP-only (no LDS round trips).
-  constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
-  for (int r = wv; r < TR; r += WPB) {
-    float amax = 0.f;
-    {
-      u32x4 v[NCL];
-#pragma unroll
-      for (int k = 0; k < NCL; ++k) {
-        const int ch = lane + 64 * k;
-        v[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int k = 0; k < NCL; ++k)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
-          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
-        }
-    }
-    amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
-    float mul, rf;
-    if (FP8) {
-      rf = amax > 0.f ? amax / 448.0f : 1.0f;
-      mul = amax > 0.f ? 448.0f / amax : 1.0f;
-    } else {
-      const int sh = f16_row_shift(amax);
-      mul = ldexpf(1.0f, sh);
-      rf = ldexpf(1.0f, -sh);
-    }
-    const bool wr = FP8 && blockIdx.x == 0 && r < T;
-    if (lane == 0) {
-      fac[r] = rf;
-      if (wr) xs[r] = rf;
-    }
-    u32x4 vr[NCL];
-#pragma unroll
-    for (int k = 0; k < NCL; ++k) {
-      const int ch = lane + 64 * k;
-      vr[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
-                       : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < NCL; ++k) {
-      const int ch = lane + 64 * k;
-      if (ch >= CPR) break;
-      uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
-      const u32x4 v = vr[k];
-      u32x4 o;
-      if (FP8) {
-        u32x2 code;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float f0 = bf16_bits_to_f32(v[2 * j] & 0xFFFFu) * mul;
-          float f1 = bf16_bits_to_f32(v[2 * j] >> 16) * mul;
-          float f2 = bf16_bits_to_f32(v[2 * j + 1] & 0xFFFFu) * mul;
-          float f3 = bf16_bits_to_f32(v[2 * j + 1] >> 16) * mul;
-          f0 = fminf(fmaxf(f0, -448.f), 448.f);
-          f1 = fminf(fmaxf(f1, -448.f), 448.f);
-          f2 = fminf(fmaxf(f2, -448.f), 448.f);
-          f3 = fminf(fmaxf(f3, -448.f), 448.f);
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
-          code[j] = (uint32_t)w;
-        }
-        if (wr) *(u32x2*)(xq + (size_t)r * H + 8 * ch) = code;
-        const u32x2 lo = fp8x4_to_f16(code.x), hi = fp8x4_to_f16(code.y);
-        o = u32x4{lo.x, lo.y, hi.x, hi.y};
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xFFFFu) * mul,
-                            bf16_bits_to_f32(v[j] >> 16) * mul);
-      }
-      *(u32x4*)pch = o;
-    }
-  }
+  convert_rows();
   // the scale runs have landed once only the code loads (and the slot load)
   // are outstanding; the code chunks are waited for one by one as the MFMAs
   // reach them.  LDS traffic done, then the barrier publishes the rows.

@@ -20,8 +20,11 @@ intermediate h or the per-slot outputs to bf16 (via torch's fp32 -> bf16 cast,
 after an fp64 -> fp32 step) to mirror where the GPU stores bf16; ``act_mode`` =
 "fp8_row" feeds the gate_up GEMM with the per-row e4m3-quantised activations.
 
-Pins: pure-Python math.fsum loops on the tiny layer; K=1 equals the dense FFN
-of the chosen expert; token permutation permutes the outputs; relabelling the
+Pins: pure-Python math.fsum loops on the tiny layer; ``bf16_bits_to_f64``
+against the bf16 closed form on all 65,536 patterns and hand-worked patterns,
+``_round_bf16`` against hand-worked ties, subnormals and overflow and a
+brute-force nearest-value search (tests/test_oracle_bf16.py); K=1 equals the
+dense FFN of the chosen expert; token permutation permutes the outputs; relabelling the
 experts leaves the output unchanged; K=E equals the softmax-weighted dense
 mixture; scale2 of down times 2**j scales the routed output by 2**j; all-zero
 codes give zero.

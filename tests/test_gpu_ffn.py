@@ -109,12 +109,69 @@ def test_fp8_arm(moe, cfg):
     assert np.array_equal(q, qo)
 
 
+@pytest.mark.parametrize("act_mode", [0, 1])
 @pytest.mark.parametrize("T", [12, 6])   # grouped path; decode path (rows converted in LDS)
-def test_fp8_zero_rows(moe, T):
+def test_zero_rows(moe, T, act_mode):
     wl = make_workload("z", T=T, H=256, E=8, K=2, I=128, has_shared=True, seed=6)
     wl.x_bf16[3] = 0
     wl.x_bf16[T - 1] = 0x8000      # -0.0
-    _full_check(moe, wl, act_mode=1, tag=f"fp8 zero rows T={T}")
+    r = _full_check(moe, wl, act_mode=act_mode, tag=f"zero rows T={T} act={act_mode}")
+    # a zero token row gives exactly zero from every expert it reaches
+    for t in (3, T - 1):
+        assert not np.any(bf16_np(r["out"][t]))
+
+
+# every e4m3 code that is not NaN (0x7F, 0xFF): zeros, subnormals 0x01-0x07,
+# normals up to 0x7E = 448, and the same with the sign bit set
+ALL_SCALE_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _all_codes_bank(wl, seed):
+    """Block scales that run through every finite e4m3 code of both signs, each
+    code on many blocks (a seeded shuffle of the cycled list)."""
+    rng = np.random.default_rng(seed)
+    for name in ("gu_scales", "dn_scales"):
+        a = getattr(wl.weights, name)
+        cyc = np.resize(ALL_SCALE_CODES, a.size)
+        setattr(wl.weights, name, rng.permutation(cyc).reshape(a.shape).astype(np.uint8))
+    return wl
+
+
+@pytest.mark.parametrize("act_mode", [0, 1])
+@pytest.mark.parametrize("T", [6, 40])   # decode path; grouped path
+def test_every_finite_e4m3_block_scale(moe, T, act_mode):
+    """Subnormal, large (products up to 6 x 448 = 2688) and negative block
+    scales, which the synthetic generator never draws, on both regimes and both
+    activation arms, at the tight gate."""
+    wl = make_workload("c", T=T, H=256, E=8, K=2, I=128, has_shared=True, seed=13,
+                       x_kind="student_t" if act_mode else "normal")
+    _all_codes_bank(wl, 13 + T)
+    for name in ("gu_scales", "dn_scales"):
+        assert set(np.unique(getattr(wl.weights, name)).tolist()) == set(ALL_SCALE_CODES.tolist())
+    _full_check(moe, wl, act_mode=act_mode, tag=f"all e4m3 scale codes T={T} act={act_mode}")
+
+
+def test_fp8_codes_written_when_no_group_is_active(moe):
+    """Every id out of range and no shared expert: no group is active, the FFN
+    computes nothing, and the row codes and scales in the workspace are still
+    the call's row quantisation of x."""
+    wl = make_workload("n", T=5, H=512, E=16, K=3, I=256, has_shared=False, seed=14,
+                       x_kind="student_t")
+    ids = torch.full((wl.T, wl.K), -1, dtype=torch.int32, device="cuda")
+    counts, offsets, sorted_slot, slot_pos, groups = moe.moe_permute(ids, wl.E, False)
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    _, ws = moe.moe_expert_ffn(W, x_dev(wl.x_bf16), wl.K, offsets, sorted_slot, groups, 1,
+                               return_ws=True)
+    torch.cuda.synchronize()
+    assert int(groups[0]) == 0
+    S = wl.T * wl.K
+    off = (S * wl.I * 2 + 255) // 256 * 256
+    q = ws[off:off + wl.T * wl.H].cpu().numpy().reshape(wl.T, wl.H)
+    off2 = off + (wl.T * wl.H + 255) // 256 * 256
+    s = ws[off2:off2 + 4 * wl.T].cpu().numpy().view(np.float32)
+    qo, so = oracle.rowquant_e4m3(bf16_bits_to_f64(wl.x_bf16).astype(np.float32))
+    assert np.array_equal(s, so)
+    assert np.array_equal(q, qo)
 
 
 @pytest.mark.parametrize("cfg", [
@@ -198,22 +255,59 @@ def test_repeated_layer_calls_are_bitwise_identical(moe):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16))
 
 
+def _whole_groups(counts, E, name):
+    """Groups whose every row is recomputed by the oracle at full size: the
+    shared group, the largest routed group, and one routed group for each size
+    of a last partial 128-row tile (1-32, 33-64, 65-96 and 97-127 rows past the
+    last full tile), so every tile shape of the grouped kernel is covered."""
+    routed = counts[:E]
+    pick = {E, int(np.argmax(routed))}
+    rem = routed % 128
+    for lo, hi in ((1, 32), (33, 64), (65, 96), (97, 127)):
+        cand = np.nonzero((rem >= lo) & (rem <= hi))[0]
+        if cand.size:
+            pick.add(int(cand[0]))
+    return sorted(pick)
+
+
 def _sampled_check(moe, name, act_mode=0, n_tok=6):
-    """Full-size run; the oracle recomputes only a sample of tokens (all their
-    routed experts and the shared expert) and the per-slot outputs of those tokens."""
+    """Full-size run.  The oracle recomputes (1) every row of a few whole groups
+    (_whole_groups) and (2) a sample of tokens: all their routed experts and the
+    shared expert, per slot and after the combine."""
     wl = workload_for(name)
     flush(f"sampled {name} T={wl.T} act={act_mode}")
     r = _run(moe, wl, act_mode)
     ids = r["ids"].cpu().numpy()
     ids_o, w_o = oracle.route_topk(wl.logits, wl.K)
     assert np.array_equal(ids, ids_o)
+    counts_o, offsets_o, sorted_o, slot_pos_o = oracle.permute(ids_o, wl.E, wl.has_shared)
+    for got, want in zip((r["counts"], r["offsets"], r["sorted_slot"], r["slot_pos"]),
+                         (counts_o, offsets_o, sorted_o, slot_pos_o)):
+        assert np.array_equal(got.cpu().numpy(), want)
     slot_pos = r["slot_pos"].cpu().numpy()
+    y_gpu = r["y_slots"]
+    x_all = bf16_bits_to_f64(wl.x_bf16)
+    xin_all = oracle.rowquant_dequant(x_all.astype(np.float32)) if act_mode else x_all
+
+    # (1) whole groups
+    groups = _whole_groups(counts_o, wl.E, name)
+    for g in groups:
+        a, b = int(offsets_o[g]), int(offsets_o[g + 1])
+        # offsets that put group g alone at positions [0, b - a), so the
+        # oracle's output holds only this group's rows
+        offs = np.zeros_like(offsets_o)
+        offs[g + 1:] = b - a
+        ref = oracle.ffn.expert_outputs(xin_all, wl.weights, wl.T, wl.K, offs, sorted_o[a:b],
+                                        h_round="bf16", groups=[g])
+        got = bf16_np(y_gpu[a:b])
+        e = normwise(got, ref)
+        flush(f"  whole group {g}: {b - a} rows ({(b - a) % 128} in the last tile)  "
+              f"y vs emul {e:.2e}")
+        assert e <= GATE_TIGHT
+
+    # (2) sampled tokens
     rng = np.random.default_rng(11)
     toks = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, n_tok, replace=False)]))
-    x = bf16_np(x_dev(wl.x_bf16)[torch.from_numpy(toks).cuda()])
-    if act_mode:
-        xq = oracle.rowquant_dequant(x.astype(np.float32))
-    y_gpu = r["y_slots"]
     cache = {}
 
     def ffn(e, rows, h_round):
@@ -225,7 +319,7 @@ def _sampled_check(moe, name, act_mode=0, n_tok=6):
     worst_y = 0.0
     out_ref = np.zeros_like(out_gpu)
     for i, t in enumerate(toks):
-        xin = xq[i:i + 1] if act_mode else x[i:i + 1]
+        xin = xin_all[t:t + 1]
         for k in range(wl.K):
             e = int(ids[t, k])
             yk = ffn(e, xin, "none")[0]
@@ -233,14 +327,12 @@ def _sampled_check(moe, name, act_mode=0, n_tok=6):
             yg = bf16_np(y_gpu[int(slot_pos[t * wl.K + k])])
             worst_y = max(worst_y, normwise(yg, ye))
             out_ref[i] += w_o[t, k] * yk
-        ys = ffn(wl.E, x[i:i + 1], "none")[0]  # shared expert: same input arm
-        if act_mode:
-            ys = ffn(wl.E, xin, "none")[0]
-        out_ref[i] += ys
+        out_ref[i] += ffn(wl.E, xin, "none")[0]    # the shared expert, same input arm
     e_out = normwise(out_gpu, out_ref)
     flush(f"  sampled {len(toks)} tokens: worst y vs emul {worst_y:.2e}  out vs oracle {e_out:.2e}")
     assert worst_y <= GATE_TIGHT
     assert e_out <= (GATE_TIGHT if not act_mode else GATE_FP8)
+    return groups
 
 
 def test_prefill_full_size_sampled(moe):
