@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     NVFP4Weights,
     moe_combine,
     moe_expert_ffn,
+    moe_expert_ffn_noalloc,
     moe_init,
     moe_layer,
     moe_permute,

@@ -41,6 +41,12 @@ int g_init_state[kMaxDevices];  // 0 = not yet, 1 = ready, < 0 = status of the f
 std::string g_init_msg[kMaxDevices];
 int g_cus[kMaxDevices];
 
+// Workspace of moe_expert_ffn_noalloc: one copy per device, held until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol; its
+// device address on each GPU is g_scratch[dev], taken once at init.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WS_BYTES];
+void* g_scratch[kMaxDevices];
+
 int ensure_init() {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -64,6 +70,18 @@ int ensure_init() {
     return rc;
   }
   g_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      int rc = e != hipSuccess ? hip_fail(e, "hipGetSymbolAddress(scratch) at init")
+                               : fail(MOE_EHIP, "hipGetSymbolAddress(scratch) returned null");
+      g_init_state[dev] = rc;
+      g_init_msg[dev] = g_err;
+      return rc;
+    }
+    g_scratch[dev] = p;
+  }
   std::vector<const void*> ks;
   moe::register_route_kernels(ks);
   moe::register_permute_kernels(ks);
@@ -209,6 +227,36 @@ int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
   hipError_t e = moe::launch_expert_ffn(*W, x, T, K, offsets, sorted_slot, groups, act_mode,
                                         y_slots, ws, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn launch");
+}
+
+int moe_expert_ffn_noalloc(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
+                           const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* groups, int act_mode, uint16_t* y_slots,
+                           void* stream) {
+  if (!W || !x || !offsets || !sorted_slot || !groups || !y_slots)
+    return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: null pointer");
+  if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
+    return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: null weight pointer");
+  if (act_mode != MOE_ACT_BF16 && act_mode != MOE_ACT_FP8_ROW)
+    return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_noalloc: unknown act_mode %d", act_mode);
+  if (!sizes_ok_common(T, W->E, K) || (W->has_shared != 0 && W->has_shared != 1))
+    return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
+  if (W->H < 256 || W->H > 4096 || W->H % 256 != 0 || W->I < 128 || W->I > 1024 || W->I % 128 != 0)
+    return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: need H a multiple of 256 in [256, 4096] and I a multiple of 128 in [128, 1024] (H=%d I=%d)", W->H, W->I);
+  const size_t need = moe::ffn_workspace_bytes(T, K, W->H, W->I, W->has_shared, act_mode);
+  if (need > (size_t)MOE_NOALLOC_WS_BYTES)
+    return fail(MOE_EWORKSPACE,
+                "moe_expert_ffn_noalloc: these sizes need %zu bytes of workspace, more than the "
+                "library's fixed %zu (use moe_expert_ffn with a caller workspace)",
+                need, (size_t)MOE_NOALLOC_WS_BYTES);
+  int rc = ensure_init();
+  if (rc != MOE_OK) return rc;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = moe::launch_expert_ffn(*W, x, T, K, offsets, sorted_slot, groups, act_mode, y_slots,
+                             g_scratch[dev], (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn_noalloc launch");
 }
 
 int moe_combine(const uint16_t* y_slots, const float* w, const int32_t* slot_pos, int T, int K,

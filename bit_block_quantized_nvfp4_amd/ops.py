@@ -18,7 +18,7 @@ from ._lib import MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_PERMU
 
 __all__ = [
     "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
-    "moe_combine", "moe_layer", "workspace_bytes", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
+    "moe_combine", "moe_layer", "workspace_bytes", "moe_expert_ffn_noalloc", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
 ]
 
 
@@ -145,6 +145,28 @@ def moe_expert_ffn(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tens
                                     _ptr(sorted_slot), _ptr(groups), act_mode, _ptr(y_slots),
                                     _ptr(ws), nb, _stream()))
     return (y_slots, ws) if return_ws else y_slots
+
+
+def moe_expert_ffn_noalloc(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tensor,
+                           sorted_slot: torch.Tensor, groups: torch.Tensor,
+                           act_mode: int = MOE_ACT_BF16, y_slots: Optional[torch.Tensor] = None):
+    """moe_expert_ffn with the library's fixed workspace (no caller workspace);
+    pass a preallocated y_slots to allocate nothing at all."""
+    _need(x, torch.bfloat16, name="x")
+    T, H = x.shape
+    if H != W.H:
+        raise ValueError("x width does not match the weight bank")
+    S = T * K + (T if W.has_shared else 0)
+    y_slots = torch.empty((S, H), dtype=torch.bfloat16, device=x.device) if y_slots is None else y_slots
+    _need(y_slots, torch.bfloat16, (S, H), "y_slots")
+    _need(offsets, torch.int32, (W.E + int(W.has_shared) + 1,), "offsets")
+    _need(sorted_slot, torch.int32, (S,), "sorted_slot")
+    _need(groups, torch.int32, (W.E + int(W.has_shared) + 1,), "groups")
+    st = W.struct()
+    check(_lib.lib().moe_expert_ffn_noalloc(ctypes.byref(st), _ptr(x), T, K, _ptr(offsets),
+                                            _ptr(sorted_slot), _ptr(groups), act_mode,
+                                            _ptr(y_slots), _stream()))
+    return y_slots
 
 
 def moe_combine(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Tensor, K: int,

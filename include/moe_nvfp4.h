@@ -191,6 +191,29 @@ int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
                    int act_mode, uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and kernels as moe_expert_ffn, with the workspace taken from a
+ * fixed array of MOE_NOALLOC_WS_BYTES inside the library (one per GPU,
+ * resolved at moe_init and held until the process ends) instead of a caller
+ * buffer.  The call allocates and frees nothing.
+ *
+ * Sizes whose moe_workspace_bytes(MOE_OP_EXPERT_FFN, ...) exceeds
+ * MOE_NOALLOC_WS_BYTES return MOE_EWORKSPACE before anything is enqueued (at
+ * H=2048, I=512, K=10 with a shared expert that is T > 2183 in the bf16 arm,
+ * T > 1926 in the FP8 arm).  Every call on one GPU uses that GPU's single
+ * array, so calls that overlap in time on one GPU (different streams, or
+ * threads without ordering) race and must not be issued; calls ordered on one
+ * stream are safe.  Nothing in the array needs to start at zero; its contents
+ * after a call are those described for moe_expert_ffn's workspace.
+ */
+#define MOE_NOALLOC_WS_BYTES (32u << 20)
+int moe_expert_ffn_noalloc(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
+                           const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* groups, int act_mode, uint16_t* y_slots,
+                           void* stream);
+
+/*
  * Combine: out[t] = bf16( sum_{k=0..K-1} w[t][k] * y_slots[slot_pos[t*K+k]]
  *                          + y_slots[slot_pos[T*K + t]] (if has_shared) ),
  * accumulated in fp32 in exactly this order (slot order, then the shared
