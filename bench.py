@@ -9,8 +9,11 @@ Headline workload: the decode/verify layer at T=8 rows (H=2048, 512 experts
 top-10 plus one shared expert, I=512).  Every step uses the next of NBANKS
 device copies of the 907.7 MB weight bank and the next of NLOGITS router-logit
 sets, so no step finds its experts in the 256 MB Infinity Cache left by the
-one before.  The same loop is then run at T=1, 2, 4 and on the prefill chunk
-(T=4096) as extra lines of the report.
+one before.  The same loop is then run at T=1, 2, 4, on the prefill chunk
+(T=4096), on the long cold prefill (T=32768, Zipf-skewed routing) and on the
+FP8-arm workload (T=8192, heavy-tailed activations) in both activation arms,
+as extra lines of the report, each with a CPU-oracle baseline on a bounded
+sample.
 
 The timed steps are captured once into a HIP graph and replayed, so the time
 is the GPU's (the library's entry points are capturable); the eager time of
@@ -184,7 +187,73 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{dt:.1f} s, numpy BLAS threads = host cores"}
 
 
+def cpu_baseline_sampled(wl, act_mode=0, budget_s=8.0):
+    """The fp64 oracle on a bounded sample of a prefill-sized layer, scaled to
+    the whole layer.
+
+    The oracle's routing and permutation run on the whole config (timed); its
+    expert FFN then runs on whole groups taken in a seeded random order (the
+    shared group first) until the budget is spent, timing the per-group
+    dequantisation and the per-row FFN apart; the combine is timed on the
+    first 512 tokens.  Whole-layer time = route/permute + n_active x mean
+    dequant + S x (FFN time per row) + combine x T/512.
+    """
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    T, K, E = wl.T, wl.K, wl.E
+    t0 = time.perf_counter()
+    ids, w = oracle.route_topk(wl.logits, K)
+    counts, offsets, sorted_slot, slot_pos = oracle.permute(ids, E, wl.has_shared)
+    t_rp = time.perf_counter() - t0
+    x = oracle.ffn.bf16_bits_to_f64(wl.x_bf16)
+    if act_mode:
+        x = oracle.rowquant_dequant(x.astype(np.float32))
+    active = [g for g in range(len(counts)) if counts[g] > 0]
+    rng = np.random.default_rng(0)
+    order = ([E] if wl.has_shared else []) + [int(g) for g in rng.permutation(
+        [g for g in active if g != E])]
+    t_dq, t_ffn, rows = [], 0.0, 0
+    t_start = time.perf_counter()
+    for g in order:
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        sl = np.asarray(sorted_slot[a:b], dtype=np.int64)
+        toks = np.where(sl < T * K, sl // K, sl - T * K)
+        t1 = time.perf_counter()
+        wg, wu, wd = oracle.ffn.dequant_expert(wl.weights, g)
+        t2 = time.perf_counter()
+        oracle.expert_ffn(x[toks], wg, wu, wd)
+        t3 = time.perf_counter()
+        t_dq.append(t2 - t1)
+        t_ffn += t3 - t2
+        rows += b - a
+        if len(t_dq) >= 3 and time.perf_counter() - t_start > budget_s:
+            break
+    n_tc = min(T, 512)
+    ysub = np.zeros((n_tc * K + n_tc, wl.H))
+    sp = np.concatenate([np.arange(n_tc * K), n_tc * K + np.arange(n_tc)])
+    t4 = time.perf_counter()
+    oracle.combine(ysub, np.asarray(w[:n_tc]), sp, n_tc, K, wl.has_shared)
+    t_cb = (time.perf_counter() - t4) * T / n_tc
+    S = int(offsets[-1])
+    full = t_rp + len(active) * float(np.mean(t_dq)) + S * t_ffn / max(rows, 1) + t_cb
+    return {"value": round(T / full, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"route+permute on all {T} tokens ({t_rp:.1f} s); {len(t_dq)} whole groups "
+                      f"({rows} rows, shared group first) for dequant and FFN; combine on "
+                      f"{n_tc} tokens; scaled to {len(active)} active groups and {S} rows: "
+                      f"{full:.1f} s per layer call"}
+
+
 COPY_BYTES = 1 << 30
+
+WORKLOAD_TEXT = {
+    "prefill": "prefill chunk: T=4096, H=2048, 512 experts top-10 + 1 shared, I=512, per-expert "
+               "logit bias N(0, 0.5)",
+    "long_prefill": "long cold prefill: T=32768, H=2048, 512 experts top-10 + 1 shared, I=512, "
+                    "Zipf(1.1)-skewed routing",
+    "fp8_arm": "FP8 arm workload: T=8192, H=2048, 512 experts top-10 + 1 shared, I=512, "
+               "Student-t(3) activations with 0.1% x1000 outliers",
+}
 
 
 def counter_pass(moe, torch, banks, base, steps):
@@ -300,6 +369,7 @@ def main():
           file=sys.stderr, flush=True)
 
     extra = {}
+    outs = {}
     if not args.no_extra:
         for T in (1, 2, 4):
             d = decode_line(T, args.steps, args.warmup)
@@ -312,26 +382,47 @@ def main():
                 "down": {"avg_us": round(d["down"]["avg_us"], 2), "GBs": round(d["down"]["GBs"], 1)},
                 "kernels": {k: round(v["avg_us"], 2) for k, v in d["kernels"].items()}}
             print(f"# decode T={T}: {d['ms_per_step'] * 1e3:.1f} us/layer", file=sys.stderr, flush=True)
-        for name in ("prefill",):
+        for name, act_mode in (("prefill", 0), ("long_prefill", 0), ("fp8_arm", 1),
+                               ("fp8_arm", 0)):
             wl = workload_for(name, with_weights=False)
             wl.weights = base.weights
             lsets = [workload_for(name, seed=s, with_weights=False).logits for s in range(2)]
-            r = LayerRunner(moe, torch, banks, wl, lsets)
+            r = LayerRunner(moe, torch, banks, wl, lsets, act_mode=act_mode)
             ms, _ = time_steps(r, torch, args.prefill_steps, 2, graph=True)
             kt = kernel_times(r, torch, moe_ops, args.prefill_steps, 2)
             S = wl.T * wl.K + wl.T
             fl_gu = 2.0 * S * H * 2 * I
             fl_dn = 2.0 * S * I * H
-            gu, dn = kt["grouped_gate_up"]["avg_us"], kt["grouped_down"]["avg_us"]
-            extra[name + f"_T{wl.T}"] = {
-                "tokens_per_s": round(wl.T / (ms / 1e3), 1), "us_per_layer": round(ms * 1e3, 1),
-                "layer_TFLOPs": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12, 1),
-                "grouped_gate_up": {"avg_us": round(gu, 1), "TFLOPs": round(fl_gu / (gu * 1e-6) / 1e12, 1),
-                                    "frac": round(fl_gu / (gu * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
-                "grouped_down": {"avg_us": round(dn, 1), "TFLOPs": round(fl_dn / (dn * 1e-6) / 1e12, 1),
-                                 "frac": round(fl_dn / (dn * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)},
-                "kernels": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
-            print(f"# {name}: {ms * 1e3:.1f} us/layer, kernels {kt}", file=sys.stderr, flush=True)
+            key = f"{name}_T{wl.T}" + ("_fp8" if act_mode else ("_bf16" if name == "fp8_arm" else ""))
+            ent = {"workload": WORKLOAD_TEXT[name] + (", FP8 row-quantised activations"
+                                                      if act_mode else ""),
+                   "tokens_per_s": round(wl.T / (ms / 1e3), 1), "us_per_layer": round(ms * 1e3, 1),
+                   "layer_TFLOPs": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12, 1),
+                   "layer_frac": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "kernels": {k: round(v["avg_us"], 2) for k, v in kt.items()}}
+            ffn_us = sum(v["avg_us"] for k, v in kt.items() if k.startswith("grouped"))
+            ent["expert_ffn"] = {"avg_us": round(ffn_us, 1),
+                                 "TFLOPs": round((fl_gu + fl_dn) / (ffn_us * 1e-6) / 1e12, 1),
+                                 "frac": round((fl_gu + fl_dn) / (ffn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            for kname, fl in (("grouped_gate_up", fl_gu), ("grouped_down", fl_dn),
+                              ("grouped_ffn", fl_gu + fl_dn)):
+                if kname in kt:
+                    us = kt[kname]["avg_us"]
+                    ent[kname] = {"avg_us": round(us, 1), "TFLOPs": round(fl / (us * 1e-6) / 1e12, 1),
+                                  "frac": round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            if name == "fp8_arm":
+                r.run(0)
+                torch.cuda.synchronize()
+                outs[act_mode] = r.out.float().clone()
+                if 0 in outs and 1 in outs:
+                    d = (outs[1] - outs[0]).abs().max() / outs[0].abs().max()
+                    extra["fp8_arm_T8192_fp8"]["vs_bf16_path_normwise"] = round(float(d), 5)
+            if not args.no_cpu:
+                ent["cpu_baseline"] = cpu_baseline_sampled(wl, act_mode)   # wl.weights: the same seed-0 bank
+            extra[key] = ent
+            print(f"# {key}: {ms * 1e3:.1f} us/layer, kernels {kt}", file=sys.stderr, flush=True)
+            del r
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -360,7 +451,14 @@ def main():
                    "global_batch": 8, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "dec_gate_up", "achieved": round(gu["GBs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "avg_us": round(gu["avg_us"], 2),
+                     "traffic": measured_traffic(),
+                     "traffic_source": "FETCH_SIZE + WRITE_SIZE per dispatch of this kernel from "
+                                       "rocprofv3 --pmc runs of bench.py --counter-pass, read from "
+                                       "the profiles/ summary while the decode kernel sources hash "
+                                       "to the value recorded there (else null); not measured in "
+                                       "this run",
+                     "layer_frac": round(head["layer_GBs"] / HBM_PEAK_GBS, 4),
+                     "avg_us": round(gu["avg_us"], 2),
                      "bytes_per_launch": int(gu["bytes"])},
         "cpu_baseline": cpu,
         "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "us_eager": round(head["ms_eager"] * 1e3, 2),

@@ -30,6 +30,7 @@ namespace moe {
 // ---------------------------------------------------------------------------
 void register_ffn_kernels(std::vector<const void*>& k) {
   register_prefill_kernels(k);
+  register_fused_kernels(k);
   register_decode_kernels(k);
 }
 
@@ -66,6 +67,8 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   float* rowfac = (float*)(wp + align256((size_t)T * H * sizeof(_Float16)));
   hipError_t e = launch_xprep(x, T, H, fp8, xh, rowfac, xq, xs, s);
   if (e != hipSuccess) return e;
+  if (fused_supported(T, H, I))
+    return launch_prefill_fused(W, T, K, offsets, sorted_slot, xh, rowfac, hbuf, y, s);
   return launch_prefill_ffn(W, T, K, offsets, sorted_slot, xh, rowfac, hbuf, y, s);
 }
 
