@@ -9,16 +9,18 @@
 //            h = bf16(silu(g * s2g * f_t) * (u * s2u * f_t)), f_t the row's
 //            epilogue factor, stored to the workspace by sorted position;
 //   down:    A = those bf16 h rows, read straight back by the same block (they
-//            are still in L2; at I = 512 the whole h tile stays in LDS for all
-//            N tiles), B = NVFP4 down rows dequantised to bf16; epilogue
-//            y = bf16(acc * s2d).
+//            are still in L2).  At I = 512 the whole h tile stays in LDS for
+//            all N tiles and is turned into f16 in place with a per-row power
+//            of two (undone in the epilogue), B = NVFP4 down rows dequantised
+//            to f16; otherwise A streams as bf16 and B is dequantised to bf16.
+//            Epilogue y = bf16(acc * f_r * s2d).
 //
-// MFMA 16x16x32 (f16 for gate_up, bf16 for down).  A block of 4 waves (one
-// per SIMD, so each wave has the whole register file of its SIMD: the
-// accumulators sit in AGPRs) owns an N tile of 512 weight rows: wave w holds
-// 8 n-blocks of 16 rows (gate_up: 64 gate rows and the 64 up rows of the same
-// pairs, so g and u of one pair sit in the same lane) against every valid
-// 16-row m-block of the tile.
+// MFMA 16x16x32 (f16 for gate_up, bf16 for down).  A block of 8 waves (two
+// per SIMD, so one wave's LDS, dequant and barrier waits overlap the other's
+// MFMAs) owns an N tile of 512 weight rows: wave w holds 4 n-blocks of 16
+// rows (gate_up: 32 gate rows and the 32 up rows of the same pairs, so g and
+// u of one pair sit in the same lane) against every valid 16-row m-block of
+// the tile.
 //
 // K runs in steps of 256 elements.  Weight codes go straight from global
 // memory into each wave's registers (only the owning wave reads them): lane
@@ -45,8 +47,9 @@ namespace moe {
 namespace {
 
 constexpr int kFK = 256;           // K elements per step
-constexpr int kFNW = 4;            // waves per block (one per SIMD)
-constexpr int kFNB = 8;            // n-blocks of 16 weight rows per wave
+constexpr int kFNW = 8;            // waves per block (two per SIMD)
+constexpr int kFNB = 4;            // n-blocks of 16 weight rows per wave
+constexpr int kFNH = kFNB / 2;     // n-blocks per weight-load half
 constexpr int kFWR = 16 * kFNB * kFNW;  // weight rows per N tile (512)
 constexpr int kFARow = 2 * kFK;    // bytes of one A row per step
 constexpr int kFSRow = kFK / 16;   // scale bytes of one weight row per step
@@ -88,6 +91,10 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
   constexpr int MB = 2 * NMB;
   constexpr int AI = NMB * 32 * kFARow / 1024 / kFNW;  // A DMA instructions per wave per step
   static_assert(!(GU && ARES), "the activation rows stream");
+  // f16 MFMA (weights dequantised with one instruction per element) for
+  // gate_up and for a resident h tile, which is turned into f16 in place;
+  // bf16 MFMA for a streamed h tile
+  constexpr bool F16 = GU || ARES;
   const int KD = GU ? H : I;
   const int nsteps = KD / kFK;
   const int NT = GU ? 2 * I / kFWR : H / kFWR;
@@ -99,29 +106,33 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
   const uint32_t rowb = (uint32_t)KD / 2, srow = (uint32_t)KD / 16;
 
   // weight row (inside the group's matrix, N tile 0) of tile row
-  // rho = 128 w + 16 nb + n: gate_up n-blocks 0-3 are gate rows, 4-7 the up
-  // rows of the same pairs
+  // rho = 16 kFNB w + 16 nb + n: for gate_up, the wave's first kFNH n-blocks
+  // are gate rows and the others the up rows of the same pairs
   auto row_of = [&](int rho) -> uint32_t {
-    const int w = rho >> 7, nb = (rho >> 4) & 7, n = rho & 15;
-    if (GU) return (uint32_t)(((nb >> 2) ? I : 0) + 64 * w + 16 * (nb & 3) + n);
+    const int w = rho / (16 * kFNB), nb = (rho / 16) % kFNB, n = rho & 15;
+    if (GU) return (uint32_t)((nb >= kFNH ? I : 0) + 16 * kFNH * w + 16 * (nb % kFNH) + n);
     return (uint32_t)rho;
   };
   // lane part of the weight offsets (n-block 0 of the wave); n-block nb adds
   // the uniform nb_off(nb)
-  const uint32_t wlane = row_of(128 * wv + m16) * rowb + 16u * q;
+  const uint32_t wlane = row_of(16 * kFNB * wv + m16) * rowb + 16u * q;
   auto nb_off = [&](int nb) -> int {
-    return (int)((row_of(128 * wv + 16 * nb) - row_of(128 * wv)) * rowb);
+    return (int)((row_of(16 * kFNB * wv + 16 * nb) - row_of(16 * kFNB * wv)) * rowb);
   };
-  // scale DMA: instructions k = wv and wv + 4 move tile rows 64 k + lane
+  // scale DMA: instruction k (k = wv, wv + kFNW, ...) moves tile rows 64 k + lane
+  constexpr int SI = kFWR * kFSRow / 1024 / kFNW;
   const uint32_t slane = row_of(64 * wv + lane) * srow;
-  const int s_hi = (int)((row_of(64 * (wv + kFNW)) - row_of(64 * wv)) * srow);  // uniform
-  // A DMA: instruction i of wave wv fills chunk positions 64 (wv + 4 i) + lane
-  // of the stage: row r = 2 (wv + 4 i) + lane / 32, chunk position lane % 32,
-  // which holds logical chunk (lane % 32) ^ (r & 15); r & 15 takes one value
-  // for even i and one for odd i.  The source offset is rowoff[r] + 16 chunk.
-  const uint32_t ach0 = 16u * (uint32_t)((lane & 31) ^ ((2 * wv + (lane >> 5)) & 15));
-  const uint32_t ach1 = 16u * (uint32_t)((lane & 31) ^ ((2 * wv + 8 + (lane >> 5)) & 15));
-  const uint32_t* rowoff_l = &sm.rowoff[2 * wv + (lane >> 5)];  // + 8 i for instruction i
+  auto s_off = [&](int i) -> int {  // uniform
+    return (int)((row_of(64 * (wv + kFNW * i)) - row_of(64 * wv)) * srow);
+  };
+  // A DMA: instruction i of wave wv fills chunk positions 64 (wv + kFNW i) +
+  // lane of the stage: row r = 2 (wv + kFNW i) + lane / 32, chunk position
+  // lane % 32, which holds logical chunk (lane % 32) ^ (r & 15).  The source
+  // offset is rowoff[r] + 16 chunk.
+  auto ach = [&](int i) -> uint32_t {
+    return 16u * (uint32_t)((lane & 31) ^ ((2 * (wv + kFNW * i) + (lane >> 5)) & 15));
+  };
+  const uint32_t* rowoff_l = &sm.rowoff[2 * wv + (lane >> 5)];  // + 2 kFNW i for instruction i
 
   // Buffer resources (every load is a 32-bit per-lane offset from a uniform
   // base, no 64-bit address registers; a read past the end returns zeros and
@@ -133,13 +144,13 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, live ? (int)bytes : 0, kBufferFlags);
   };
 
-  // weight codes of n-blocks [nb0, nb0 + 4) for N tile j, step s (both
+  // weight codes of n-blocks [nb0, nb0 + kFNH) for N tile j, step s (both
   // 64-byte halves of each row's 128-byte line, back to back)
-  auto load_w = [&](u32x4 (&w)[4][2], int nb0, int j, int s, bool live) {
+  auto load_w = [&](u32x4 (&w)[kFNH][2], int nb0, int j, int s, bool live) {
     const __amdgpu_buffer_rsrc_t rw = rsrc(codes_g, wbytes, live);
     const int so = j * NTROWS * (int)rowb + kFSRow * 8 * s;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kFNH; ++nb)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         w[nb][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)wlane + 64 * c, so + nb_off(nb0 + nb), 0);
@@ -150,16 +161,16 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
     for (int i = 0; i < AI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)&sm.A[st][1024 * (wv + kFNW * i)], 16,
-          (int)(rowoff_l[8 * i] + ((i & 1) ? ach1 : ach0)), kFARow * s, 0, 0);
+          (int)(rowoff_l[2 * kFNW * i] + ach(i)), kFARow * s, 0, 0);
   };
   auto dma_s = [&](int j, int s, int st, bool live) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(scales_g, sbytes, live);
     const int so = j * NTROWS * (int)srow + kFSRow * s;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)&sm.S[st][1024 * (wv + kFNW * i)], 16,
-          (int)slane, so + i * s_hi, 0, 0);
+          (int)slane, so + s_off(i), 0, 0);
   };
 
   // A operand of m-block mb, sub-MFMA (c, jj): row 16 mb + m16, logical chunk
@@ -169,25 +180,26 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
   for (int jj = 0; jj < 4; ++jj) aoff[jj] = (uint32_t)(m16 * kFARow + 16 * ((4 * q + jj) ^ m16));
 
   f32x4 acc[MB][kFNB];
-  // n-blocks [nb0, nb0 + 4) over the whole step: per k-block, the A operands
-  // of every m-block, then per n-block one dequantised B operand and its MFMAs
-  auto compute = [&](const u32x4 (&w)[4][2], int nb0, int st) {
+  // n-blocks [nb0, nb0 + kFNH) over the whole step: per k-block, the A
+  // operands of every m-block, then per n-block one dequantised B operand
+  // and its MFMAs
+  auto compute = [&](const u32x4 (&w)[kFNH][2], int nb0, int st) {
     const uint8_t* Ab = sm.A[st];
-    const uint8_t* Sb = sm.S[st] + (128 * wv + 16 * nb0 + m16) * kFSRow + 2 * q;
+    const uint8_t* Sb = sm.S[st] + (16 * kFNB * wv + 16 * nb0 + m16) * kFSRow + 2 * q;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      uint32_t sp[4];
+      uint32_t sp[kFNH];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sp[nb] = *(const uint16_t*)(Sb + 16 * kFSRow * nb + 8 * c);
+      for (int nb = 0; nb < kFNH; ++nb) sp[nb] = *(const uint16_t*)(Sb + 16 * kFSRow * nb + 8 * c);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         u32x4 a[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) a[mb] = *(const u32x4*)(Ab + aoff[jj] + mb * 16 * kFARow + 256 * c);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < kFNH; ++nb) {
           u32x4 b;
-          if (GU) {
+          if (F16) {
             const f16x2 sv = e4m3x2_to_f16(sp[nb]);
             b = __builtin_bit_cast(u32x4, dqh8(w[nb][c][jj], jj < 2 ? sv.x : sv.y));
           } else {
@@ -196,7 +208,7 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
           }
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            if (GU)
+            if (F16)
               acc[mb][nb0 + nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                   __builtin_bit_cast(f16x8, a[mb]), __builtin_bit_cast(f16x8, b), acc[mb][nb0 + nb], 0, 0, 0);
             else
@@ -212,11 +224,11 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
 
   // One step from stage st, with no branch inside.  Step s + 1 (if any; else
   // the same loads against size-0 resources) is requested meanwhile: its A
-  // tile and scales first (into the other stage), then the weights of
-  // n-blocks 0-3 once this step has consumed them, then those of n-blocks
-  // 4-7; the closing wait leaves only those last 8 weight loads in flight
-  // (their first use is half-way through the next step).
-  u32x4 wlo[4][2], whi[4][2];
+  // tile and scales first (into the other stage), then the weights of the
+  // wave's first kFNH n-blocks once this step has consumed them, then those
+  // of the others; the closing wait leaves only those last 2 kFNH weight
+  // loads in flight (their first use is half-way through the next step).
+  u32x4 wlo[kFNH][2], whi[kFNH][2];
   const int total = NT * nsteps;
   auto step = [&](int j, int s, int st) {
     const int gs = j * nsteps + s;
@@ -226,19 +238,47 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
     dma_s(jn, sn, st ^ 1, more);
     compute(wlo, 0, st);
     load_w(wlo, 0, jn, sn, more);
-    compute(whi, 4, st);
-    load_w(whi, 4, jn, sn, more);
-    fused_wait_vmcnt<8>();  // (n-blocks 4-7: 4 x 2 loads)
+    compute(whi, kFNH, st);
+    load_w(whi, kFNH, jn, sn, more);
+    fused_wait_vmcnt<2 * kFNH>();
     __syncthreads();        // every wave's DMA has landed; stage st is free again
   };
 
   load_w(wlo, 0, 0, 0, true);
-  load_w(whi, 4, 0, 0, true);
+  load_w(whi, kFNH, 0, 0, true);
   dma_a(0, 0, true);
   if (ARES) dma_a(1, 1, true);
   dma_s(0, 0, 0, true);
   fused_wait_vmcnt<0>();
   __syncthreads();
+  if (ARES) {
+    // The resident bf16 h rows -> f16 in place, each row times the power of
+    // two that brings its absmax into [2^14, 2^15) (exact for every value
+    // above 2^-29 of the row's absmax), undone in the epilogue through
+    // row_fac.  Row r's 512 elements are its 512-byte slices of the two
+    // stages; lane l holds 16 bytes of stage l / 32 (the chunk swizzle does
+    // not matter to an elementwise pass).
+    for (int r = wv; r < MB * 16; r += kFNW) {
+      uint8_t* p = &sm.A[lane >> 5][r * kFARow + 16 * (lane & 31)];
+      const u32x4 v = *(const u32x4*)p;
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k] & 0xFFFFu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k] >> 16)));
+      }
+      amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
+      const int sh = f16_row_shift(amax);
+      const float mul = ldexpf(1.0f, sh);
+      if (lane == 0) sm.row_fac[r] = ldexpf(1.0f, -sh);
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = pack_f16x2(bf16_bits_to_f32(v[k] & 0xFFFFu) * mul, bf16_bits_to_f32(v[k] >> 16) * mul);
+      *(u32x4*)p = o;
+    }
+    __syncthreads();
+  }
   for (int j = 0; j < NT; ++j) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -266,9 +306,9 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
           if (r < ti.rows && sm.row_ok[r + z]) {
             const float f = sm.row_fac[r + z];
 #pragma unroll
-            for (int np = 0; np < kFNB / 2; ++np) {
-              const int col = NTROWS * j + 64 * wv + 16 * np + m16;
-              const float g = acc[mb][np][v] * s2g * f, u = acc[mb][kFNB / 2 + np][v] * s2u * f;
+            for (int np = 0; np < kFNH; ++np) {
+              const int col = NTROWS * j + 16 * kFNH * wv + 16 * np + m16;
+              const float g = acc[mb][np][v] * s2g * f, u = acc[mb][kFNH + np][v] * s2u * f;
               out[(size_t)(p0 + r) * I + col] = f32_to_bf16_bits(silu_f32(g) * u);
             }
           }
@@ -281,10 +321,11 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
         for (int v = 0; v < 4; ++v) {
           const int r = 16 * mb + 4 * q + v;
           if (r < ti.rows && sm.row_ok[r + z]) {
+            const float f = ARES ? sm.row_fac[r + z] : 1.0f;
 #pragma unroll
             for (int nb = 0; nb < kFNB; ++nb) {
-              const int col = NTROWS * j + 128 * wv + 16 * nb + m16;
-              out[(size_t)(p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][v] * s2d);
+              const int col = NTROWS * j + 16 * kFNB * wv + 16 * nb + m16;
+              out[(size_t)(p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][v] * f * s2d);
             }
           }
         }
