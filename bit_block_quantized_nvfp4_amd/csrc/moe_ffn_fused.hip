@@ -26,8 +26,8 @@
 // memory into each wave's registers (only the owning wave reads them): lane
 // (n = l%16, q = l/16) loads bytes [64c + 16q, +16) of its row's 128-byte step
 // slice for c = 0, 1, so each load instruction covers 64 contiguous bytes of
-// 16 rows and the two instructions of a row complete its 128-byte line back
-// to back (no line is left half-read for a later step).  The step's A tile
+// 16 rows, and both halves of every 128-byte line are requested within the
+// same step.  The step's A tile
 // (valid rows x 512 B) and block scales (512 rows x 16 B) go to a
 // double-buffered LDS stage by global->LDS DMA; everything for step s+1 is
 // issued before step s computes; one wait and one barrier per step.  A rows
@@ -49,7 +49,7 @@ namespace {
 constexpr int kFK = 256;           // K elements per step
 constexpr int kFNW = 8;            // waves per block (two per SIMD)
 constexpr int kFNB = 4;            // n-blocks of 16 weight rows per wave
-constexpr int kFNH = kFNB / 2;     // n-blocks per weight-load half
+constexpr int kFNH = kFNB / 2;     // gate (or up) n-blocks of a gate_up wave
 constexpr int kFWR = 16 * kFNB * kFNW;  // weight rows per N tile (512)
 constexpr int kFARow = 2 * kFK;    // bytes of one A row per step
 constexpr int kFSRow = kFK / 16;   // scale bytes of one weight row per step
@@ -115,13 +115,18 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
   };
   // lane part of the weight offsets (n-block 0 of the wave); n-block nb adds
   // the uniform nb_off(nb)
-  const uint32_t wlane = row_of(16 * kFNB * wv + m16) * rowb + 16u * q;
+  // (the per-lane offsets below are functions of the lane id, re-derived in
+  // every step from an opaque copy of it instead of being held in registers
+  // across the whole K loop)
+  auto wlane_of = [&](int ln) -> uint32_t {
+    return row_of(16 * kFNB * wv + (ln & 15)) * rowb + 16u * (uint32_t)(ln >> 4);
+  };
   auto nb_off = [&](int nb) -> int {
     return (int)((row_of(16 * kFNB * wv + 16 * nb) - row_of(16 * kFNB * wv)) * rowb);
   };
   // scale DMA: instruction k (k = wv, wv + kFNW, ...) moves tile rows 64 k + lane
   constexpr int SI = kFWR * kFSRow / 1024 / kFNW;
-  const uint32_t slane = row_of(64 * wv + lane) * srow;
+  auto slane_of = [&](int ln) -> uint32_t { return row_of(64 * wv + ln) * srow; };
   auto s_off = [&](int i) -> int {  // uniform
     return (int)((row_of(64 * (wv + kFNW * i)) - row_of(64 * wv)) * srow);
   };
@@ -129,10 +134,9 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
   // lane of the stage: row r = 2 (wv + kFNW i) + lane / 32, chunk position
   // lane % 32, which holds logical chunk (lane % 32) ^ (r & 15).  The source
   // offset is rowoff[r] + 16 chunk.
-  auto ach = [&](int i) -> uint32_t {
-    return 16u * (uint32_t)((lane & 31) ^ ((2 * (wv + kFNW * i) + (lane >> 5)) & 15));
+  auto ach = [&](int ln, int i) -> uint32_t {
+    return 16u * (uint32_t)((ln & 31) ^ ((2 * (wv + kFNW * i) + (ln >> 5)) & 15));
   };
-  const uint32_t* rowoff_l = &sm.rowoff[2 * wv + (lane >> 5)];  // + 2 kFNW i for instruction i
 
   // Buffer resources (every load is a 32-bit per-lane offset from a uniform
   // base, no 64-bit address registers; a read past the end returns zeros and
@@ -144,26 +148,27 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
     return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, live ? (int)bytes : 0, kBufferFlags);
   };
 
-  // weight codes of n-blocks [nb0, nb0 + kFNH) for N tile j, step s (both
-  // 64-byte halves of each row's 128-byte line, back to back)
-  auto load_w = [&](u32x4 (&w)[kFNH][2], int nb0, int j, int s, bool live) {
+  // weight codes of chunk c (bytes [64c, 64c + 64) of each row's 128-byte
+  // step slice) of all the wave's n-blocks, for N tile j, step s
+  auto load_w = [&](u32x4 (&w)[kFNB], int c, int j, int s, bool live, int ln) {
+    const uint32_t wlane = wlane_of(ln);
     const __amdgpu_buffer_rsrc_t rw = rsrc(codes_g, wbytes, live);
     const int so = j * NTROWS * (int)rowb + kFSRow * 8 * s;
 #pragma unroll
-    for (int nb = 0; nb < kFNH; ++nb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        w[nb][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)wlane + 64 * c, so + nb_off(nb0 + nb), 0);
+    for (int nb = 0; nb < kFNB; ++nb)
+      w[nb] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)wlane + 64 * c, so + nb_off(nb), 0);
   };
-  auto dma_a = [&](int s, int st, bool live) {
+  auto dma_a = [&](int s, int st, bool live, int ln) {
+    const uint32_t* rowoff_l = &sm.rowoff[2 * wv + (ln >> 5)];  // + 2 kFNW i for instruction i
     const __amdgpu_buffer_rsrc_t ra = rsrc(abase, abytes, live);
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)&sm.A[st][1024 * (wv + kFNW * i)], 16,
-          (int)(rowoff_l[2 * kFNW * i] + ach(i)), kFARow * s, 0, 0);
+          (int)(rowoff_l[2 * kFNW * i] + ach(ln, i)), kFARow * s, 0, 0);
   };
-  auto dma_s = [&](int j, int s, int st, bool live) {
+  auto dma_s = [&](int j, int s, int st, bool live, int ln) {
+    const uint32_t slane = slane_of(ln);
     const __amdgpu_buffer_rsrc_t rs = rsrc(scales_g, sbytes, live);
     const int so = j * NTROWS * (int)srow + kFSRow * s;
 #pragma unroll
@@ -175,80 +180,84 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
 
   // A operand of m-block mb, sub-MFMA (c, jj): row 16 mb + m16, logical chunk
   // 16 c + 4 q + jj, stored at chunk (4 q + jj) ^ m16 of the row's half c
-  uint32_t aoff[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) aoff[jj] = (uint32_t)(m16 * kFARow + 16 * ((4 * q + jj) ^ m16));
+  auto aoff_of = [&](int ln, int jj) -> uint32_t {
+    return (uint32_t)((ln & 15) * kFARow + 16 * ((4 * (ln >> 4) + jj) ^ (ln & 15)));
+  };
 
   f32x4 acc[MB][kFNB];
-  // n-blocks [nb0, nb0 + kFNH) over the whole step: per k-block, the A
-  // operands of every m-block, then per n-block one dequantised B operand
-  // and its MFMAs
-  auto compute = [&](const u32x4 (&w)[kFNH][2], int nb0, int st) {
-    const uint8_t* Ab = sm.A[st];
-    const uint8_t* Sb = sm.S[st] + (16 * kFNB * wv + 16 * nb0 + m16) * kFSRow + 2 * q;
+  // Chunk c of the step (k-blocks 4c .. 4c + 3).  Per k-block, the A
+  // operands of every m-block (each read feeds all kFNB n-blocks), then per
+  // n-block its dequantised B operand and MFMAs.  The B operands rotate
+  // through 3 register slots, so a dequant never overwrites an operand that a
+  // queued MFMA has yet to read; the other wave on the SIMD covers the LDS
+  // latency at the start of each k-block.
+  auto compute = [&](const u32x4 (&w)[kFNB], int c, int st, int ln) {
+    const uint8_t* Ab = sm.A[st] + 256 * c;
+    const uint8_t* Sb = sm.S[st] + (16 * kFNB * wv + (ln & 15)) * kFSRow + 2 * (ln >> 4) + 8 * c;
+    uint32_t sp[kFNB];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t sp[kFNH];
+    for (int nb = 0; nb < kFNB; ++nb) sp[nb] = *(const uint16_t*)(Sb + 16 * kFSRow * nb);
+    u32x4 bq[3];
 #pragma unroll
-      for (int nb = 0; nb < kFNH; ++nb) sp[nb] = *(const uint16_t*)(Sb + 16 * kFSRow * nb + 8 * c);
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x4 a[MB];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x4 a[MB];
+      for (int mb = 0; mb < MB; ++mb) a[mb] = *(const u32x4*)(Ab + aoff_of(ln, jj) + mb * 16 * kFARow);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) a[mb] = *(const u32x4*)(Ab + aoff[jj] + mb * 16 * kFARow + 256 * c);
-#pragma unroll
-        for (int nb = 0; nb < kFNH; ++nb) {
-          u32x4 b;
-          if (F16) {
-            const f16x2 sv = e4m3x2_to_f16(sp[nb]);
-            b = __builtin_bit_cast(u32x4, dqh8(w[nb][c][jj], jj < 2 ? sv.x : sv.y));
-          } else {
-            const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[nb], 1.0f, false);
-            b = __builtin_bit_cast(u32x4, dq8(w[nb][c][jj], jj < 2 ? sv.x : sv.y));
-          }
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            if (F16)
-              acc[mb][nb0 + nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  __builtin_bit_cast(f16x8, a[mb]), __builtin_bit_cast(f16x8, b), acc[mb][nb0 + nb], 0, 0, 0);
-            else
-              acc[mb][nb0 + nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b), acc[mb][nb0 + nb], 0, 0, 0);
-          }
+      for (int nb = 0; nb < kFNB; ++nb) {
+        u32x4& b = bq[(kFNB * jj + nb) % 3];
+        if (F16) {
+          const f16x2 sv = e4m3x2_to_f16(sp[nb]);
+          b = __builtin_bit_cast(u32x4, dqh8(w[nb][jj], jj < 2 ? sv.x : sv.y));
+        } else {
+          const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sp[nb], 1.0f, false);
+          b = __builtin_bit_cast(u32x4, dq8(w[nb][jj], jj < 2 ? sv.x : sv.y));
         }
-        // one k-block at a time: bounds the operands in flight
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if (F16)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, a[mb]), __builtin_bit_cast(f16x8, b), acc[mb][nb], 0, 0, 0);
+          else
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b), acc[mb][nb], 0, 0, 0);
+        }
+        if (nb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
+      // one k-block at a time: bounds the operands in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // One step from stage st, with no branch inside.  Step s + 1 (if any; else
   // the same loads against size-0 resources) is requested meanwhile: its A
-  // tile and scales first (into the other stage), then the weights of the
-  // wave's first kFNH n-blocks once this step has consumed them, then those
-  // of the others; the closing wait leaves only those last 2 kFNH weight
-  // loads in flight (their first use is half-way through the next step).
-  u32x4 wlo[kFNH][2], whi[kFNH][2];
+  // tile and scales first (into the other stage), then the weights of chunk 0
+  // once this step has consumed them, then those of chunk 1; the closing wait
+  // leaves only those last kFNB weight loads in flight (their first use is
+  // half-way through the next step).
+  u32x4 w0[kFNB], w1[kFNB];
   const int total = NT * nsteps;
   auto step = [&](int j, int s, int st) {
+    int ln = (int)(threadIdx.x & 63);
+    asm volatile("" : "+v"(ln));
     const int gs = j * nsteps + s;
     const bool more = gs + 1 < total;
     const int jn = s + 1 < nsteps ? j : j + 1, sn = s + 1 < nsteps ? s + 1 : 0;
-    if (!ARES) dma_a(sn, st ^ 1, more);
-    dma_s(jn, sn, st ^ 1, more);
-    compute(wlo, 0, st);
-    load_w(wlo, 0, jn, sn, more);
-    compute(whi, kFNH, st);
-    load_w(whi, kFNH, jn, sn, more);
-    fused_wait_vmcnt<2 * kFNH>();
-    __syncthreads();        // every wave's DMA has landed; stage st is free again
+    if (!ARES) dma_a(sn, st ^ 1, more, ln);
+    dma_s(jn, sn, st ^ 1, more, ln);
+    compute(w0, 0, st, ln);
+    load_w(w0, 0, jn, sn, more, ln);
+    compute(w1, 1, st, ln);
+    load_w(w1, 1, jn, sn, more, ln);
+    fused_wait_vmcnt<kFNB>();
+    __syncthreads();  // every wave's DMA has landed; stage st is free again
   };
 
-  load_w(wlo, 0, 0, 0, true);
-  load_w(whi, kFNH, 0, 0, true);
-  dma_a(0, 0, true);
-  if (ARES) dma_a(1, 1, true);
-  dma_s(0, 0, 0, true);
+  load_w(w0, 0, 0, 0, true, lane);
+  load_w(w1, 1, 0, 0, true, lane);
+  dma_a(0, 0, true, lane);
+  if (ARES) dma_a(1, 1, true, lane);
+  dma_s(0, 0, 0, true, lane);
   fused_wait_vmcnt<0>();
   __syncthreads();
   if (ARES) {
