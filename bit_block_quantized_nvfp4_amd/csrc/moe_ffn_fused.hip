@@ -215,12 +215,14 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
+          // weights as the MFMA's A operand, tokens as B: the lane holding
+          // token column t gets 4 consecutive output features of it
           if (F16)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(f16x8, a[mb]), __builtin_bit_cast(f16x8, b), acc[mb][nb], 0, 0, 0);
+                __builtin_bit_cast(f16x8, b), __builtin_bit_cast(f16x8, a[mb]), acc[mb][nb], 0, 0, 0);
           else
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, b), acc[mb][nb], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a[mb]), acc[mb][nb], 0, 0, 0);
         }
         if (nb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
@@ -305,39 +307,46 @@ __device__ __forceinline__ void fused_phase(FfnSmem& sm, const PfTile& ti,
     // of being hoisted out of it into registers
     int p0 = ti.p0, z = 0;
     asm volatile("" : "+s"(p0), "+s"(z));
+    // acc[mb][nb][v]: token row r = 16 mb + (lane % 16), output feature
+    // 16 nb + 4 (lane / 16) + v of the wave's n-blocks: 4 consecutive
+    // features per lane, stored as one 8-byte write
+    const int ln = (int)(threadIdx.x & 63);
+    const int r16 = ln & 15, g4 = 4 * (ln >> 4);
     if (GU) {
       const float s2g = scale2[3 * e + 0], s2u = scale2[3 * e + 1];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = 16 * mb + r16;
+        if (r < ti.rows && sm.row_ok[r + z]) {
+          const float f = sm.row_fac[r + z];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = 16 * mb + 4 * q + v;
-          if (r < ti.rows && sm.row_ok[r + z]) {
-            const float f = sm.row_fac[r + z];
+          for (int np = 0; np < kFNH; ++np) {
+            const int col = NTROWS * j + 16 * kFNH * wv + 16 * np + g4;
+            float hv[4];
 #pragma unroll
-            for (int np = 0; np < kFNH; ++np) {
-              const int col = NTROWS * j + 16 * kFNH * wv + 16 * np + m16;
+            for (int v = 0; v < 4; ++v) {
               const float g = acc[mb][np][v] * s2g * f, u = acc[mb][kFNH + np][v] * s2u * f;
-              out[(size_t)(p0 + r) * I + col] = f32_to_bf16_bits(silu_f32(g) * u);
+              hv[v] = silu_f32(g) * u;
             }
+            *(u32x2*)(out + (size_t)(p0 + r) * I + col) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
           }
         }
+      }
     } else {
       const float s2d = scale2[3 * e + 2];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = 16 * mb + r16;
+        if (r < ti.rows && sm.row_ok[r + z]) {
+          const float f = (ARES ? sm.row_fac[r + z] : 1.0f) * s2d;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = 16 * mb + 4 * q + v;
-          if (r < ti.rows && sm.row_ok[r + z]) {
-            const float f = ARES ? sm.row_fac[r + z] : 1.0f;
-#pragma unroll
-            for (int nb = 0; nb < kFNB; ++nb) {
-              const int col = NTROWS * j + 16 * kFNB * wv + 16 * nb + m16;
-              out[(size_t)(p0 + r) * H + col] = f32_to_bf16_bits(acc[mb][nb][v] * f * s2d);
-            }
+          for (int nb = 0; nb < kFNB; ++nb) {
+            const int col = NTROWS * j + 16 * kFNB * wv + 16 * nb + g4;
+            const f32x4 v = acc[mb][nb];
+            *(u32x2*)(out + (size_t)(p0 + r) * H + col) = u32x2{pack_bf16x2(v[0] * f, v[1] * f), pack_bf16x2(v[2] * f, v[3] * f)};
           }
         }
+      }
     }
   }
 }
