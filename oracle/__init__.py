@@ -25,6 +25,10 @@ Sources (the web pages this layer is described on):
 * [tp2]    issue "EXL3 Qwen3.8-Flash-Next on CUDA sm_120: expert offload, TP=2,
            graphs and MTP", section on expert offload: per-slot expert outputs
            summed in the same order as one rank; Questions item 2.
+* [nsys]   same issue, the per-kernel table of the prefill profile: the router
+           runs as a w4a16 GEMM.
+* [fp4local] same issue, the FP4-Local section: the only dequant kernel left is
+           the router dequant.
 * [OCP]    the OCP Microscaling Formats (MX) v1.0 and OCP 8-bit floating point
            specifications, which define the e2m1 and e4m3 ("fn") encodings the
            pages name.
@@ -43,3 +47,4 @@ from .route import route_topk  # noqa: F401
 from .permute import permute  # noqa: F401
 from .ffn import silu, expert_ffn, expert_outputs, combine, moe_layer  # noqa: F401
 from .fp8 import rowquant_e4m3, rowquant_dequant  # noqa: F401
+from .router import router_logits, router_route, sigmoid  # noqa: F401

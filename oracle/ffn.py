@@ -11,9 +11,11 @@ Definitions:
 * y = h . W_down^T;
 * the shared expert (index E) is one more group that holds every token with
   weight 1 (reading: the pages give it no gate);
-* combine: out[t] = sum_{k<K} w[t,k] * y[slot_pos[t*K+k]] + y_shared[t]
+* combine: out[t] = sum_{k<K} w[t,k] * y[slot_pos[t*K+k]] + s_t * y_shared[t]
   ([attr]: weighted sum; [tp2]: the per-slot outputs are summed in one fixed
-  order -- the oracle sums in fp64, so its order does not matter here).
+  order -- the oracle sums in fp64, so its order does not matter here), s_t = 1,
+  or sigmoid of the shared-gate logit when the router has a gate row (see
+  router.py for that reading).
 
 Options for diagnostics only: ``h_round``/``y_round`` = "bf16" round the
 intermediate h or the per-slot outputs to bf16 (via torch's fp32 -> bf16 cast,
@@ -99,14 +101,21 @@ def expert_outputs(xin: np.ndarray, bank, T: int, K: int, offsets, sorted_slot,
 
 
 def combine(y_slots: np.ndarray, w: np.ndarray, slot_pos: np.ndarray, T: int, K: int,
-            has_shared: bool) -> np.ndarray:
+            has_shared: bool, shared_gate=None) -> np.ndarray:
+    """out[t] = sum_k w[t,k] y[slot_pos[t*K+k]] + s_t y[slot_pos[T*K+t]], with
+    s_t = sigmoid(shared_gate[t]) when gate logits are given, else 1."""
+    from .router import sigmoid
+
     sp_all = np.asarray(slot_pos, dtype=np.int64)
     sp = sp_all[:T * K].reshape(T, K)
     out = np.zeros((T, y_slots.shape[1]), dtype=np.float64)
     for k in range(K):
         out += w[:, k:k + 1] * y_slots[sp[:, k]]
     if has_shared:
-        out += y_slots[sp_all[T * K:T * K + T]]
+        ys = y_slots[sp_all[T * K:T * K + T]]
+        if shared_gate is not None:
+            ys = sigmoid(np.asarray(shared_gate, dtype=np.float64))[:, None] * ys
+        out += ys
     return out
 
 

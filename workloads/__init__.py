@@ -9,7 +9,10 @@ from .generators import (  # noqa: F401
     CONFIGS,
     DECODE_TS,
     MoEWorkload,
+    ROUTER_SCALE2,
+    RouterBank,
     WeightBank,
+    make_router,
     make_weights,
     make_workload,
     workload_for,

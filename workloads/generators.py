@@ -34,6 +34,11 @@ SCALE_CODE_HI = 72  # e4m3 code of 2**2
 
 # Stream ids for SeedSequence children; fixed so tensors never share a stream.
 _S_X, _S_LOGITS, _S_BIAS, _S_PERM, _S_GU, _S_GUS, _S_DN, _S_DNS, _S_OUTL, _S_T = range(10)
+_S_RC, _S_RS = 10, 11
+
+# scale2 of a synthetic router matrix: with uniform e2m1 codes and block scales
+# 2^-4 .. 4, an N(0,1) row of H = 2048 gives logits of standard deviation ~1
+ROUTER_SCALE2 = 2.0 ** -8
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -103,6 +108,27 @@ def make_weights(E: int, H: int, I: int, has_shared: bool, seed: int = 0,
                                       size=(n, H, I // 16), dtype=np.uint8)
     s2 = np.full((n, 3), scale2, dtype=np.float32)
     return WeightBank(E, H, I, has_shared, gu, gus, dn, dns, s2)
+
+
+@dataclass
+class RouterBank:
+    """NVFP4 router matrix: rows 0..E-1 route to the experts; with has_gate,
+    row E is the shared-expert gate."""
+    E: int
+    H: int
+    has_gate: bool
+    codes: np.ndarray    # uint8 [R, H/2], R = E + has_gate
+    scales: np.ndarray   # uint8 [R, H/16]
+    scale2: float
+
+
+def make_router(E: int, H: int, has_gate: bool, seed: int = 0,
+                scale2: float = ROUTER_SCALE2) -> RouterBank:
+    R = E + (1 if has_gate else 0)
+    codes = _rng(seed, _S_RC).integers(0, 256, size=(R, H // 2), dtype=np.uint8)
+    scales = _rng(seed, _S_RS).integers(SCALE_CODE_LO, SCALE_CODE_HI + 1, size=(R, H // 16),
+                                        dtype=np.uint8)
+    return RouterBank(E, H, has_gate, codes, scales, float(np.float32(scale2)))
 
 
 def _normal_x(seed: int, T: int, H: int) -> np.ndarray:
