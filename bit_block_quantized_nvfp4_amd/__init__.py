@@ -6,13 +6,16 @@ The compute path is the HIP library ``libmoe_nvfp4.so`` (C ABI in
 from .ops import (  # noqa: F401
     MOE_ACT_BF16,
     MOE_ACT_FP8_ROW,
+    NVFP4Router,
     NVFP4Weights,
     moe_combine,
+    moe_combine_gated,
     moe_expert_ffn,
     moe_expert_ffn_noalloc,
     moe_init,
     moe_layer,
     moe_permute,
     moe_route_topk,
+    moe_router_topk,
     workspace_bytes,
 )

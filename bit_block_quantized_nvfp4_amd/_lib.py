@@ -37,6 +37,17 @@ class MoeNvfp4Weights(ctypes.Structure):
     ]
 
 
+class MoeNvfp4Router(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("scale2", ctypes.c_float),
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("has_gate", ctypes.c_int32),
+    ]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"moe_nvfp4 status {status}: {msg}")
@@ -59,6 +70,8 @@ _SIGS = {
     "moe_expert_ffn_noalloc": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _P, _I,
                                     _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_combine_gated": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_router_topk": (_I, [ctypes.POINTER(MoeNvfp4Router), _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_timing_enable": (_I, [_I]),
     "moe_timing_reset": (_I, []),
     "moe_timing_read": (_I, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),

@@ -84,6 +84,7 @@ int ensure_init() {
   }
   std::vector<const void*> ks;
   moe::register_route_kernels(ks);
+  moe::register_router_kernels(ks);
   moe::register_permute_kernels(ks);
   moe::register_combine_kernels(ks);
   moe::register_ffn_kernels(ks);
@@ -267,8 +268,40 @@ int moe_combine(const uint16_t* y_slots, const float* w, const int32_t* slot_pos
     return fail(MOE_EINVAL, "moe_combine: need T >= 1, 1 <= K <= 32, H a positive multiple of 8, has_shared in {0,1}");
   int rc = ensure_init();
   if (rc != MOE_OK) return rc;
-  hipError_t e = moe::launch_combine(y_slots, w, slot_pos, T, K, H, has_shared, out, (hipStream_t)stream);
+  hipError_t e = moe::launch_combine(y_slots, w, slot_pos, nullptr, T, K, H, has_shared, out,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "moe_combine launch");
+}
+
+int moe_combine_gated(const uint16_t* y_slots, const float* w, const int32_t* slot_pos,
+                      const float* gate, int T, int K, int H, uint16_t* out, void* stream) {
+  if (!y_slots || !w || !slot_pos || !gate || !out)
+    return fail(MOE_EINVAL, "moe_combine_gated: null pointer");
+  if (T < 1 || K < 1 || K > 32 || H < 8 || H % 8 != 0 || (long long)T * K > (1LL << 30))
+    return fail(MOE_EINVAL, "moe_combine_gated: need T >= 1, 1 <= K <= 32, H a positive multiple of 8");
+  int rc = ensure_init();
+  if (rc != MOE_OK) return rc;
+  hipError_t e = moe::launch_combine(y_slots, w, slot_pos, gate, T, K, H, 1, out, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_combine_gated launch");
+}
+
+int moe_router_topk(const moe_nvfp4_router* R, const uint16_t* x, int T, int K, int32_t* ids,
+                    float* w, float* logits, float* gate, void* stream) {
+  if (!R || !x || !ids || !w) return fail(MOE_EINVAL, "moe_router_topk: null pointer");
+  if (!R->codes || !R->scales) return fail(MOE_EINVAL, "moe_router_topk: null weight pointer");
+  if (R->has_gate != 0 && R->has_gate != 1)
+    return fail(MOE_EINVAL, "moe_router_topk: has_gate must be 0 or 1");
+  if (R->has_gate && !gate)
+    return fail(MOE_EINVAL, "moe_router_topk: the matrix has a gate row but gate is NULL");
+  if (!sizes_ok_common(T, R->E, K))
+    return fail(MOE_EINVAL, "moe_router_topk: need T >= 1, 1 <= K <= min(E, 32), E <= 1024 (T=%d E=%d K=%d)", T, R->E, K);
+  if (R->H < 256 || R->H > 8192 || R->H % 256 != 0 || (long long)T * R->H >= (1LL << 30))
+    return fail(MOE_EINVAL, "moe_router_topk: need H a multiple of 256 in [256, 8192] and T*H < 2^30 (T=%d H=%d)", T, R->H);
+  int rc = ensure_init();
+  if (rc != MOE_OK) return rc;
+  hipError_t e = moe::launch_router_topk(*R, x, T, K, ids, w, logits, R->has_gate ? gate : nullptr,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_router_topk launch");
 }
 
 int moe_timing_enable(int on) {

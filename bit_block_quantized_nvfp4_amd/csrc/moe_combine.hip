@@ -1,5 +1,5 @@
-// Combine (A10): out[t] = bf16( sum_k w[t][k] * y[slot_pos[t*K+k]] + y[slot_pos[T*K+t]] ),
-// fp32 accumulation in slot order then the shared expert, one rounding at the
+// Combine (A10): out[t] = bf16( sum_k w[t][k] * y[slot_pos[t*K+k]] + c_t y[slot_pos[T*K+t]] ),
+// c_t = 1, or sigmoid(gate[t]) for the gated shared expert; fp32 accumulation in slot order then the shared expert, one rounding at the
 // end.  The order is fixed per element and independent of how the grid is cut
 // (the same-order rule for per-slot expert outputs of the issue "EXL3
 // Qwen3.8-Flash-Next on CUDA sm_120 ...", expert-parallel TP=2).
@@ -11,7 +11,8 @@ namespace moe {
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const float* __restrict__ w,
-                                                 const int32_t* __restrict__ slot_pos, int T,
+                                                 const int32_t* __restrict__ slot_pos,
+                                                 const float* __restrict__ gate, int T,
                                                  int K, int H, int has_shared,
                                                  uint16_t* __restrict__ out) {
   const int cpr = H / 8;  // 8-column chunks per row
@@ -51,10 +52,19 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   }
   if (ps >= 0 && ps < TK + T) {
     const u32x4 v = *(const u32x4*)(y + (size_t)ps * H + 8 * c);
+    if (gate) {  // sigmoid-gated shared expert
+      const float sg = 1.0f / (1.0f + expf(-gate[t]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += bf16_bits_to_f32(v[j] & 0xFFFFu);
-      acc[2 * j + 1] += bf16_bits_to_f32(v[j] >> 16);
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(sg, bf16_bits_to_f32(v[j] & 0xFFFFu), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(sg, bf16_bits_to_f32(v[j] >> 16), acc[2 * j + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += bf16_bits_to_f32(v[j] & 0xFFFFu);
+        acc[2 * j + 1] += bf16_bits_to_f32(v[j] >> 16);
+      }
     }
   }
   u32x4 o;
@@ -65,11 +75,12 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
 
 void register_combine_kernels(std::vector<const void*>& k) { k.push_back((const void*)&k_combine); }
 
-hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos, int T,
-                          int K, int H, int has_shared, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos,
+                          const float* gate, int T, int K, int H, int has_shared, uint16_t* out,
+                          hipStream_t s) {
   const long n = (long)T * (H / 8);
   MOE_LAUNCH("combine", s, k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, w,
-             slot_pos, T, K, H, has_shared, out);
+             slot_pos, gate, T, K, H, has_shared, out);
   return hipGetLastError();
 }
 

@@ -41,8 +41,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_share
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                           int32_t* slot_pos, int32_t* groups, void* ws, hipStream_t s);
 
-hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos, int T,
-                          int K, int H, int has_shared, uint16_t* out, hipStream_t s);
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* slot_pos,
+                          const float* gate, int T, int K, int H, int has_shared, uint16_t* out,
+                          hipStream_t s);
+
+void register_router_kernels(std::vector<const void*>& k);
+hipError_t launch_router_topk(const moe_nvfp4_router& R, const uint16_t* x, int T, int K,
+                              int32_t* ids, float* w, float* logits, float* gate, hipStream_t s);
 
 size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode);
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,

@@ -12,107 +12,18 @@
 // counts the j with s_j > s_b or s_j == s_b and j < b).  The weights are the
 // softmax of the K selected logits (equal to the renormalised full softmax),
 // computed in fp32 with a fixed-order DPP sum.
-#include <limits.h>
-#include <math.h>
-
-#include "moe_device.hpp"
 #include "moe_internal.hpp"
+#include "moe_topk.hpp"
 
 namespace moe {
-
-// Order-preserving 32-bit key of a logit: larger logit -> larger key; NaN was
-// replaced by -inf; -0 is folded onto +0 so that equal logits have equal keys.
-__device__ __forceinline__ uint32_t logit_key(float v) {
-  const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_logit(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// wave_max_u32 (moe_device.hpp) gives the max; the min below is used only on
-// an exact tie.
-// Min over the 64 lanes (the tie case only): quad and row steps as above,
-// then readlane of lanes 0, 16, 32, 48.
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp<0xB1>(v));
-  v = min(v, dpp<0x4E>(v));
-  v = min(v, dpp<0x141>(v));
-  v = min(v, dpp<0x140>(v));
-  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return min(a, b);
-}
 
 template <int MAXV>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T,
                                                      int E, int K, int32_t* __restrict__ ids,
                                                      float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
-  const float* row = logits + (size_t)t * E;
-
-  uint32_t key[MAXV], jx[MAXV];  // key and slot j (expert lane + 64 j) of each entry
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int e = lane + 64 * j;
-    float z = -INFINITY;
-    if (e < E) z = row[e];
-    // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
-    key[j] = (e < E) ? logit_key((z != z) ? -INFINITY : z) : 0u;
-    jx[j] = (uint32_t)j;
-  }
-  // largest key first; a swap only on a strictly larger key keeps equal keys
-  // in ascending j, i.e. ascending expert index
-#pragma unroll
-  for (int pass = 0; pass < MAXV; ++pass) {
-#pragma unroll
-    for (int i = pass & 1; i + 1 < MAXV; i += 2) {
-      const bool sw = key[i + 1] > key[i];
-      const uint32_t k0 = key[i], k1 = key[i + 1], j0 = jx[i], j1 = jx[i + 1];
-      key[i] = sw ? k1 : k0;
-      key[i + 1] = sw ? k0 : k1;
-      jx[i] = sw ? j1 : j0;
-      jx[i + 1] = sw ? j0 : j1;
-    }
-  }
-
-  float zsel = -INFINITY;
-  int isel = 0;
-  for (int k = 0; k < K; ++k) {
-    const uint32_t kmax = wave_max_u32(key[0]);
-    const bool has = key[0] == kmax;
-    const unsigned long long m = __ballot(has);
-    int win;  // expert index of the winner
-    if (__popcll(m) == 1) {
-      const int wl = __ffsll((long long)m) - 1;
-      win = wl + 64 * __builtin_amdgcn_readlane((int)jx[0], wl);
-    } else {
-      win = (int)wave_min_u32(has ? (uint32_t)lane + 64u * jx[0] : 0xFFFFFFFFu);
-    }
-    if (lane == k) {
-      zsel = key_logit(kmax);
-      isel = win;
-    }
-    if (lane == (win & 63)) {  // pop the head: the next largest becomes the head
-#pragma unroll
-      for (int i = 0; i + 1 < MAXV; ++i) {
-        key[i] = key[i + 1];
-        jx[i] = jx[i + 1];
-      }
-      key[MAXV - 1] = 0u;
-    }
-  }
-
-  const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zsel), 0));
-  float ex = 0.f;
-  if (lane < K) ex = expf(zsel == z0 ? 0.f : zsel - z0);
-  const float sum = wave_sum_dpp(ex);
-  if (lane < K) {
-    ids[(size_t)t * K + lane] = isel;
-    w[(size_t)t * K + lane] = ex / sum;
-  }
+  route_row_topk<MAXV>(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K);
 }
 
 void register_route_kernels(std::vector<const void*>& k) {

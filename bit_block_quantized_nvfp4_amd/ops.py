@@ -19,6 +19,7 @@ from ._lib import MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_PERMU
 __all__ = [
     "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
     "moe_combine", "moe_layer", "workspace_bytes", "moe_expert_ffn_noalloc", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
+    "NVFP4Router", "moe_router_topk", "moe_combine_gated",
 ]
 
 
@@ -73,6 +74,30 @@ class NVFP4Weights:
                                     self.scale2.data_ptr(), self.E, H, I, int(self.has_shared))
 
 
+@dataclass
+class NVFP4Router:
+    """A device-resident NVFP4 router matrix in the layout of moe_nvfp4_router:
+    E expert rows, plus the shared-expert gate row at index E when has_gate."""
+    codes: torch.Tensor   # uint8 [E + has_gate, H/2]
+    scales: torch.Tensor  # uint8 [E + has_gate, H/16]
+    scale2: float
+    E: int
+    H: int
+    has_gate: bool
+
+    @classmethod
+    def from_bank(cls, rb, device="cuda") -> "NVFP4Router":
+        return cls(torch.from_numpy(rb.codes).to(device), torch.from_numpy(rb.scales).to(device),
+                   float(rb.scale2), rb.E, rb.H, bool(rb.has_gate))
+
+    def struct(self) -> _lib.MoeNvfp4Router:
+        R = self.E + int(self.has_gate)
+        _need(self.codes, torch.uint8, (R, self.H // 2), "router codes")
+        _need(self.scales, torch.uint8, (R, self.H // 16), "router scales")
+        return _lib.MoeNvfp4Router(self.codes.data_ptr(), self.scales.data_ptr(), self.scale2,
+                                   self.E, self.H, int(self.has_gate))
+
+
 def moe_init() -> None:
     check(_lib.lib().moe_init())
 
@@ -100,6 +125,33 @@ def moe_route_topk(logits: torch.Tensor, K: int, ids: Optional[torch.Tensor] = N
     _need(w, torch.float32, (T, K), "w")
     check(_lib.lib().moe_route_topk(_ptr(logits), T, E, K, _ptr(ids), _ptr(w), _stream()))
     return ids, w
+
+
+def moe_router_topk(R: NVFP4Router, x: torch.Tensor, K: int, want_logits: bool = False,
+                    ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                    logits: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
+    """Router GEMM + top-K.  Returns (ids, w, logits or None, gate logits or None)."""
+    _need(x, torch.bfloat16, name="x")
+    T, H = x.shape
+    if H != R.H:
+        raise ValueError("x width does not match the router matrix")
+    dev = x.device
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, K), dtype=torch.float32, device=dev) if w is None else w
+    _need(ids, torch.int32, (T, K), "ids")
+    _need(w, torch.float32, (T, K), "w")
+    if want_logits and logits is None:
+        logits = torch.empty((T, R.E), dtype=torch.float32, device=dev)
+    if logits is not None:
+        _need(logits, torch.float32, (T, R.E), "logits")
+    if R.has_gate and gate is None:
+        gate = torch.empty((T,), dtype=torch.float32, device=dev)
+    if gate is not None:
+        _need(gate, torch.float32, (T,), "gate")
+    st = R.struct()
+    check(_lib.lib().moe_router_topk(ctypes.byref(st), _ptr(x), T, K, _ptr(ids), _ptr(w),
+                                     _ptr(logits), _ptr(gate), _stream()))
+    return ids, w, logits, (gate if R.has_gate else None)
 
 
 def moe_permute(ids: torch.Tensor, E: int, has_shared: bool, ws: Optional[torch.Tensor] = None,
@@ -180,6 +232,22 @@ def moe_combine(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Tensor, 
     _need(out, torch.bfloat16, (T, H), "out")
     check(_lib.lib().moe_combine(_ptr(y_slots), _ptr(w), _ptr(slot_pos), T, K, H, int(has_shared),
                                  _ptr(out), _stream()))
+    return out
+
+
+def moe_combine_gated(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Tensor,
+                      gate: torch.Tensor, K: int, out: Optional[torch.Tensor] = None):
+    """Combine with the shared expert scaled by sigmoid(gate[t])."""
+    _need(y_slots, torch.bfloat16, name="y_slots")
+    _need(w, torch.float32, name="w")
+    T = w.shape[0]
+    H = y_slots.shape[1]
+    _need(slot_pos, torch.int32, (T * K + T,), "slot_pos")
+    _need(gate, torch.float32, (T,), "gate")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=y_slots.device) if out is None else out
+    _need(out, torch.bfloat16, (T, H), "out")
+    check(_lib.lib().moe_combine_gated(_ptr(y_slots), _ptr(w), _ptr(slot_pos), _ptr(gate), T, K, H,
+                                       _ptr(out), _stream()))
     return out
 
 

@@ -5,6 +5,8 @@
  * One layer call is four entry points, run in this order on one HIP stream:
  *
  *   moe_route_topk  -> ids, w          router softmax + top-K per token
+ *                                      (or moe_router_topk: router GEMM from
+ *                                      NVFP4 weights fused with the top-K)
  *   moe_permute     -> counts, offsets, sorted_slot, slot_pos
  *   moe_expert_ffn  -> y_slots         gate_up GEMM, SiLU*up, down GEMM per
  *                                      expert group (routed + shared)
@@ -127,6 +129,49 @@ int moe_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float
                    void* stream);
 
 /*
+ * An NVFP4 router matrix: R = E + has_gate rows of H, the same encoding as
+ * the experts (listed as a w4a16 GEMM, 4-bit weights against 16-bit
+ * activations, in the nsys kernel table of the issue "[job]
+ * Qwen3.8-Flash-Next: long-context cold prefill to SGLang parity").  Rows
+ * 0..E-1 give the expert logits; row E, when has_gate, gives the logit of the
+ * shared expert's sigmoid gate.
+ *
+ *   codes  [R][H/2]   e2m1 codes, low nibble = even K index
+ *   scales [R][H/16]  e4m3 scale of each 16 consecutive K
+ *   scale2            fp32 scale of the whole matrix
+ */
+typedef struct moe_nvfp4_router {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  float scale2;
+  int32_t E;
+  int32_t H;
+  int32_t has_gate;
+} moe_nvfp4_router;
+
+/*
+ * Router gating GEMM fused with the top-K (the issue above names the router's
+ * gating GEMM and its top-k as the first prefill op that moves the logits):
+ *
+ *   z[t][e] = scale2 * sum_k x[t][k] * e2m1(code[e][k]) * e4m3(scale[e][k/16])
+ *
+ * accumulated in f32 (order unspecified; |error| <= H * 2^-24 * sum_k |terms|),
+ * then ids / w of each token exactly as moe_route_topk computes them from z.
+ *
+ *   R       host struct of device pointers, see moe_nvfp4_router
+ *   x       [T][H] bf16 bit patterns                  (in)
+ *   ids     [T][K] int32, w [T][K] float32            (out) as moe_route_topk
+ *   logits  [T][E] float32, or NULL                   (out) z, when wanted
+ *   gate    [T] float32 (required iff R->has_gate)    (out) row E's logit
+ *
+ * Limits: H a multiple of 256 in [256, 8192], 1 <= K <= min(E, 32),
+ * E <= 1024, T * H < 2^30.  Rows are independent; the ids are those of
+ * moe_route_topk applied to the returned logits, bit for bit.
+ */
+int moe_router_topk(const moe_nvfp4_router* R, const uint16_t* x, int T, int K, int32_t* ids,
+                    float* w, float* logits, float* gate, void* stream);
+
+/*
  * Group the T*K routed slots (slot s = t*K + k) by expert.
  *
  *   ids         [T][K] int32, each in [0, E)   (in)
@@ -230,6 +275,21 @@ int moe_expert_ffn_noalloc(const moe_nvfp4_weights* W, const uint16_t* x, int T,
  */
 int moe_combine(const uint16_t* y_slots, const float* w, const int32_t* slot_pos, int T, int K,
                 int H, int has_shared, uint16_t* out, void* stream);
+
+/*
+ * Combine with a gated shared expert: as moe_combine with has_shared = 1,
+ * except that the shared expert's row is scaled by sigmoid(gate[t]) =
+ * 1 / (1 + exp(-gate[t])) (fp32) before it is added:
+ *
+ *   out[t] = bf16( sum_k w[t][k] * y[slot_pos[t*K+k]] + sigmoid(gate[t]) * y[slot_pos[T*K+t]] )
+ *
+ * in that order.  gate [T] float32 is the router's row-E logit
+ * (moe_router_topk's `gate`).  The pages name a shared expert next to the
+ * routed ones but do not print its gate; this entry point covers the common
+ * sigmoid-gated form, moe_combine the ungated one.
+ */
+int moe_combine_gated(const uint16_t* y_slots, const float* w, const int32_t* slot_pos,
+                      const float* gate, int T, int K, int H, uint16_t* out, void* stream);
 
 /*
  * Per-kernel timing, for measurement only.  While enabled, every kernel the
