@@ -287,7 +287,7 @@ int moe_combine_gated(const uint16_t* y_slots, const float* w, const int32_t* sl
 
 int moe_router_topk(const moe_nvfp4_router* R, const uint16_t* x, int T, int K, int32_t* ids,
                     float* w, float* logits, float* gate, void* stream) {
-  if (!R || !x || !ids || !w) return fail(MOE_EINVAL, "moe_router_topk: null pointer");
+  if (!R || !x || !ids || !w || !logits) return fail(MOE_EINVAL, "moe_router_topk: null pointer");
   if (!R->codes || !R->scales) return fail(MOE_EINVAL, "moe_router_topk: null weight pointer");
   if (R->has_gate != 0 && R->has_gate != 1)
     return fail(MOE_EINVAL, "moe_router_topk: has_gate must be 0 or 1");

@@ -127,10 +127,10 @@ def moe_route_topk(logits: torch.Tensor, K: int, ids: Optional[torch.Tensor] = N
     return ids, w
 
 
-def moe_router_topk(R: NVFP4Router, x: torch.Tensor, K: int, want_logits: bool = False,
+def moe_router_topk(R: NVFP4Router, x: torch.Tensor, K: int,
                     ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
                     logits: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
-    """Router GEMM + top-K.  Returns (ids, w, logits or None, gate logits or None)."""
+    """Router GEMM + top-K.  Returns (ids, w, logits, gate logits or None)."""
     _need(x, torch.bfloat16, name="x")
     T, H = x.shape
     if H != R.H:
@@ -140,10 +140,8 @@ def moe_router_topk(R: NVFP4Router, x: torch.Tensor, K: int, want_logits: bool =
     w = torch.empty((T, K), dtype=torch.float32, device=dev) if w is None else w
     _need(ids, torch.int32, (T, K), "ids")
     _need(w, torch.float32, (T, K), "w")
-    if want_logits and logits is None:
-        logits = torch.empty((T, R.E), dtype=torch.float32, device=dev)
-    if logits is not None:
-        _need(logits, torch.float32, (T, R.E), "logits")
+    logits = torch.empty((T, R.E), dtype=torch.float32, device=dev) if logits is None else logits
+    _need(logits, torch.float32, (T, R.E), "logits")
     if R.has_gate and gate is None:
         gate = torch.empty((T,), dtype=torch.float32, device=dev)
     if gate is not None:

@@ -156,12 +156,13 @@ typedef struct moe_nvfp4_router {
  *   z[t][e] = scale2 * sum_k x[t][k] * e2m1(code[e][k]) * e4m3(scale[e][k/16])
  *
  * accumulated in f32 (order unspecified; |error| <= H * 2^-24 * sum_k |terms|),
- * then ids / w of each token exactly as moe_route_topk computes them from z.
+ * then ids / w of each token exactly as moe_route_topk computes them from z
+ * (two kernels: the GEMM writes z, the router's top-K reads it back).
  *
  *   R       host struct of device pointers, see moe_nvfp4_router
  *   x       [T][H] bf16 bit patterns                  (in)
  *   ids     [T][K] int32, w [T][K] float32            (out) as moe_route_topk
- *   logits  [T][E] float32, or NULL                   (out) z, when wanted
+ *   logits  [T][E] float32                            (out) z
  *   gate    [T] float32 (required iff R->has_gate)    (out) row E's logit
  *
  * Limits: H a multiple of 256 in [256, 8192], 1 <= K <= min(E, 32),

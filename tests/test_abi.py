@@ -60,16 +60,17 @@ def test_argument_errors_are_reported_without_a_gpu(lib):
     assert cg(one, one, one, one, 4, 2, 12, one, None) == L.MOE_EINVAL        # H % 8
     rt = lib.moe_router_topk
     R = L.MoeNvfp4Router(16, 16, 1.0, 64, 512, 1)
-    assert rt(ctypes.byref(R), one, 4, 2, one, one, None, None, None) == L.MOE_EINVAL  # gate row, no gate
-    assert rt(ctypes.byref(R), one, 4, 65, one, one, None, one, None) == L.MOE_EINVAL  # K > E
+    assert rt(ctypes.byref(R), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL   # gate row, no gate
+    assert rt(ctypes.byref(R), one, 4, 65, one, one, one, one, None) == L.MOE_EINVAL   # K > E
+    assert rt(ctypes.byref(R), one, 4, 2, one, one, None, one, None) == L.MOE_EINVAL   # no logits
     Rh = L.MoeNvfp4Router(16, 16, 1.0, 64, 300, 0)                                   # H % 256
-    assert rt(ctypes.byref(Rh), one, 4, 2, one, one, None, None, None) == L.MOE_EINVAL
+    assert rt(ctypes.byref(Rh), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL
     Rb = L.MoeNvfp4Router(16, 16, 1.0, 64, 16384, 0)                                 # H > 8192
-    assert rt(ctypes.byref(Rb), one, 4, 2, one, one, None, None, None) == L.MOE_EINVAL
+    assert rt(ctypes.byref(Rb), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL
     Rn = L.MoeNvfp4Router(0, 16, 1.0, 64, 512, 0)                                    # null codes
-    assert rt(ctypes.byref(Rn), one, 4, 2, one, one, None, None, None) == L.MOE_EINVAL
+    assert rt(ctypes.byref(Rn), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL
     Rg = L.MoeNvfp4Router(16, 16, 1.0, 64, 512, 2)                                   # has_gate 2
-    assert rt(ctypes.byref(Rg), one, 4, 2, one, one, None, one, None) == L.MOE_EINVAL
+    assert rt(ctypes.byref(Rg), one, 4, 2, one, one, one, one, None) == L.MOE_EINVAL
 
 
 def test_workspace_sizes(lib):

@@ -34,12 +34,12 @@ def _check_router(moe, x_bits, rb, K, tag):
     flush(f"router {tag}: T={x_bits.shape[0]} H={rb.H} E={rb.E} K={K} gate={rb.has_gate}")
     R = moe.NVFP4Router.from_bank(rb)
     x = x_dev(x_bits)
-    ids, w, z, g = moe.moe_router_topk(R, x, K, want_logits=True)
-    ids2, w2, z2, g2 = moe.moe_router_topk(R, x, K)   # no logits output: same routing
+    ids, w, z, g = moe.moe_router_topk(R, x, K)
+    ids2, w2, z2, g2 = moe.moe_router_topk(R, x, K)   # a second call: bitwise the same
     torch.cuda.synchronize()
-    assert z2 is None
     ids, w, z = ids.cpu().numpy(), w.cpu().numpy(), z.cpu().numpy()
     assert np.array_equal(ids, ids2.cpu().numpy()) and np.array_equal(w, w2.cpu().numpy())
+    assert np.array_equal(z, z2.cpu().numpy())
 
     z_ref = oracle.router_logits(x_bits, rb.codes, rb.scales, rb.scale2)
     absw = np.abs(dequant_nvfp4(rb.codes, rb.scales, rb.scale2))
@@ -66,7 +66,7 @@ def _check_router(moe, x_bits, rb, K, tag):
     return ids, w, z, g
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "fp8_arm"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "long_prefill", "fp8_arm"])
 def test_router_on_configs(moe, name):
     Ts = DECODE_TS if name == "decode" else (None,)
     for T in Ts:
@@ -82,6 +82,11 @@ def test_router_on_configs(moe, name):
     (513, 2048, 33, 10, True),   # one past the 512 tile (the 1024-expert kernel)
     (1024, 256, 5, 32, True),    # maximum E and K
     (64, 8192, 3, 4, False),     # maximum H
+    (1000, 512, 1024, 12, True), # largest T of the split-K kernel
+    (100, 512, 1100, 6, True),   # 32-token tiled kernel: ragged T, E a multiple of 4
+    (513, 256, 8200, 10, True),  # 64-token tiled kernel: E % 4 = 1, three expert tiles
+    (1024, 256, 2000, 32, True), # tiled kernel at the maximum E and K
+    (8, 8192, 1030, 2, False),   # tiled kernel at the maximum H and the smallest E
 ])
 def test_router_edges(moe, E, H, T, K, gate):
     wl = make_workload("r", T=T, H=H, E=E, K=K, I=128, has_shared=gate, seed=5,
