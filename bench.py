@@ -1,9 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 routed-MoE layer on one MI355X.
 
-A step is one whole layer call -- moe_route_topk, moe_permute, moe_expert_ffn
-(gate_up + SiLU + down, routed experts and the shared expert), moe_combine --
-over one batch of synthetic tokens already resident in HBM.
+A step is one whole layer call -- router top-K, permutation, expert FFN
+(gate_up + SiLU + down, routed experts and the shared expert) and combine,
+through moe_route_permute and moe_expert_ffn_combine (for decode batches one
+and two kernels: the top-K and permutation share a block, the combine runs in
+the down kernel's tail) -- over one batch of synthetic tokens already
+resident in HBM.  The same step through the four separate entry points is
+timed beside it (us_unfused).
 
 Headline workload: the decode/verify layer at T=8 rows (H=2048, 512 experts
 top-10 plus one shared expert, I=512).  Every step uses the next of NBANKS
@@ -80,9 +84,9 @@ def _down_bytes(H, I):
 class LayerRunner:
     """Pre-allocated buffers for one workload; run(step) enqueues one layer call."""
 
-    def __init__(self, moe, torch, banks, wl, logits_sets, act_mode=0):
+    def __init__(self, moe, torch, banks, wl, logits_sets, act_mode=0, fused=True):
         self.moe, self.torch = moe, torch
-        self.banks, self.wl, self.act_mode = banks, wl, act_mode
+        self.banks, self.wl, self.act_mode, self.fused = banks, wl, act_mode, fused
         dev = "cuda"
         T, K, E, H = wl.T, wl.K, wl.E, wl.H
         hs = wl.has_shared
@@ -98,8 +102,8 @@ class LayerRunner:
                      torch.empty(G + 1, dtype=i32, device=dev))
         self.ws_p = torch.empty(max(1, moe.workspace_bytes(1, T, E, K, 0, 0, hs)), dtype=torch.uint8,
                                 device=dev)
-        self.ws_f = torch.empty(moe.workspace_bytes(2, T, E, K, H, wl.I, hs, act_mode),
-                                dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(moe.workspace_bytes(3, T, E, K, H, wl.I, hs, act_mode),
+                                dtype=torch.uint8, device=dev)   # enough for either path
         self.y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.distinct = []
@@ -108,6 +112,13 @@ class LayerRunner:
         moe = self.moe
         W = self.banks[step % len(self.banks)]
         lg = self.logits[step % len(self.logits)]
+        if self.fused:   # moe_route_permute + moe_expert_ffn_combine: the same results
+            moe.moe_route_permute(lg, self.wl.K, self.wl.has_shared, self.ws_p,
+                                  (self.ids, self.w) + self.perm)
+            moe.moe_expert_ffn_combine(W, self.x, self.wl.K, self.perm[1], self.perm[2],
+                                       self.perm[4], self.w, self.perm[3], self.act_mode,
+                                       ws=self.ws_f, y_slots=self.y, out=self.out)
+            return
         moe.moe_route_topk(lg, self.wl.K, self.ids, self.w)
         moe.moe_permute(self.ids, self.wl.E, self.wl.has_shared, self.ws_p, self.perm)
         moe.moe_expert_ffn(W, self.x, self.wl.K, self.perm[1], self.perm[2], self.perm[4],
@@ -345,6 +356,9 @@ def main():
         r = LayerRunner(moe, torch, banks, wl, lsets)
         ms, wall = time_steps(r, torch, steps, warmup, graph=True)
         ms_eager, _ = time_steps(r, torch, steps, warmup, graph=False)
+        r.fused = False
+        ms_unfused, _ = time_steps(r, torch, steps, warmup, graph=True)
+        r.fused = True
         kt = kernel_times(r, torch, moe_ops, steps, warmup)
         act = r.active_groups()
         n_act = float(np.mean(act))
@@ -355,7 +369,8 @@ def main():
                        + T * wl.E * 4)
         gu = kt["dec_gate_up"]
         dn = kt["dec_down"]
-        return dict(T=T, ms_per_step=ms, ms_eager=ms_eager, wall_s=wall, tokens_per_s=T / (ms / 1e3),
+        return dict(T=T, ms_per_step=ms, ms_eager=ms_eager, ms_unfused=ms_unfused, wall_s=wall,
+                    tokens_per_s=T / (ms / 1e3),
                     active_groups=n_act, layer_bytes=layer_bytes,
                     layer_GBs=layer_bytes / (ms / 1e3) / 1e9, kernels=kt,
                     gate_up=dict(bytes=gu_bytes, avg_us=gu["avg_us"],
@@ -376,6 +391,7 @@ def main():
             extra[f"decode_T{T}"] = {
                 "tokens_per_s": round(d["tokens_per_s"], 1), "us_per_layer": round(d["ms_per_step"] * 1e3, 2),
                 "us_per_layer_eager": round(d["ms_eager"] * 1e3, 2),
+                "us_per_layer_unfused": round(d["ms_unfused"] * 1e3, 2),
                 "layer_GBs": round(d["layer_GBs"], 1),
                 "gate_up": {"avg_us": round(d["gate_up"]["avg_us"], 2), "GBs": round(d["gate_up"]["GBs"], 1),
                             "frac": round(d["gate_up"]["GBs"] / HBM_PEAK_GBS, 4)},
@@ -462,7 +478,10 @@ def main():
                      "bytes_per_launch": int(gu["bytes"])},
         "cpu_baseline": cpu,
         "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "us_eager": round(head["ms_eager"] * 1e3, 2),
-                  "timing": "HIP graph replay of the timed steps (eager time: us_eager)",
+                  "us_unfused": round(head["ms_unfused"] * 1e3, 2),
+                  "timing": "HIP graph replay of the timed steps (eager time: us_eager); the step "
+                            "is moe_route_permute + moe_expert_ffn_combine (us_unfused: the four "
+                            "separate entry points, same results)",
                   "GBs": round(head["layer_GBs"], 1),
                   "frac": round(head["layer_GBs"] / HBM_PEAK_GBS, 4),
                   "active_groups": round(head["active_groups"], 2),

@@ -11,10 +11,12 @@ from .ops import (  # noqa: F401
     moe_combine,
     moe_combine_gated,
     moe_expert_ffn,
+    moe_expert_ffn_combine,
     moe_expert_ffn_noalloc,
     moe_init,
     moe_layer,
     moe_permute,
+    moe_route_permute,
     moe_route_topk,
     moe_router_topk,
     workspace_bytes,

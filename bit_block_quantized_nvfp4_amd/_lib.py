@@ -20,6 +20,7 @@ MOE_ACT_BF16 = 0
 MOE_ACT_FP8_ROW = 1
 MOE_OP_PERMUTE = 1
 MOE_OP_EXPERT_FFN = 2
+MOE_OP_EXPERT_FFN_COMBINE = 3
 MOE_NOALLOC_WS_BYTES = 32 << 20
 
 
@@ -70,6 +71,9 @@ _SIGS = {
     "moe_expert_ffn_noalloc": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _P, _I,
                                     _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_route_permute": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn_combine": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _P, _I,
+                                    _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine_gated": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_router_topk": (_I, [ctypes.POINTER(MoeNvfp4Router), _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_timing_enable": (_I, [_I]),

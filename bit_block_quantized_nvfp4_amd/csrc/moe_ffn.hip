@@ -72,4 +72,23 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   return launch_prefill_ffn(W, T, K, offsets, sorted_slot, xh, rowfac, hbuf, y, s);
 }
 
+// The expert FFN followed by the combine kernel, as one call.  (Folding the
+// combine into the decode down kernel -- the last block of each column slice
+// combining it after the others publish their rows -- was measured slower:
+// publishing across the XCDs' L2 caches costs a write-back per block, more
+// than the combine launch it saves.)
+size_t ffn_combine_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode) {
+  return ffn_workspace_bytes(T, K, H, I, has_shared, act_mode);
+}
+
+hipError_t launch_expert_ffn_combine(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                                     const int32_t* offsets, const int32_t* sorted_slot,
+                                     const int32_t* groups, int act_mode, const float* w,
+                                     const int32_t* slot_pos, const float* gate,
+                                     uint16_t* y_slots, uint16_t* out, void* ws, hipStream_t s) {
+  hipError_t e = launch_expert_ffn(W, x, T, K, offsets, sorted_slot, groups, act_mode, y_slots, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_combine(y_slots, w, slot_pos, gate, T, K, W.H, W.has_shared ? 1 : 0, out, s);
+}
+
 }  // namespace moe

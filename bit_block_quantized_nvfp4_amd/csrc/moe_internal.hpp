@@ -37,6 +37,13 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* 
                              hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int K);
+// Batches up to this many tokens (one per wave) are routed and permuted by
+// one block.
+constexpr int kRouteFuseMaxT = 4;
+hipError_t launch_route_permute(const float* logits, int T, int E, int K, int has_shared,
+                                int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups, void* ws,
+                                hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_shared,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
                           int32_t* slot_pos, int32_t* groups, void* ws, hipStream_t s);
@@ -54,6 +61,13 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
                              const int32_t* offsets, const int32_t* sorted_slot,
                              const int32_t* groups, int act_mode, uint16_t* y_slots, void* ws,
                              hipStream_t s);
+
+size_t ffn_combine_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode);
+hipError_t launch_expert_ffn_combine(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                                     const int32_t* offsets, const int32_t* sorted_slot,
+                                     const int32_t* groups, int act_mode, const float* w,
+                                     const int32_t* slot_pos, const float* gate,
+                                     uint16_t* y_slots, uint16_t* out, void* ws, hipStream_t s);
 
 // Decode/prefill switch of moe_expert_ffn: T <= kDecodeMaxT uses the GEMV path.
 constexpr int kDecodeMaxT = 8;

@@ -18,6 +18,7 @@
 // uses to find the expert of a work unit with one load.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
+#include "moe_topk.hpp"
 
 namespace moe {
 
@@ -26,6 +27,7 @@ constexpr int kChunk = 256;           // slots ranked at once
 constexpr int kTileSlots = 4 * kChunk;
 constexpr int kSmallSlots = 2048;
 constexpr int kMaxE = 1024;
+static_assert(kRouteFuseMaxT * 32 <= kSmallSlots, "the fused batch fits the one-block permutation");
 
 // Exclusive scan, in place, of a[0..n) held in LDS, by a 256-thread block.
 // Returns the total.  Must be called by every thread of the block.
@@ -119,22 +121,25 @@ __device__ void write_shared_group(int T, int TK, int off_shared, int32_t* __res
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_permute_small(
-    const int32_t* __restrict__ ids, int T, int E, int K, int has_shared,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
-    int32_t* __restrict__ groups) {
-  __shared__ unsigned long long masks[kBlock / 64][kMaxE];
-  __shared__ int run[kMaxE + 2];
-  __shared__ int wsum[kBlock / 64];
+// Count, scan and scatter of all T*K slots by one 256-thread block.  `ids`
+// may be global or LDS memory; masks and run are the block's LDS.  With
+// init == true the LDS set-up is done here, else the caller has done it.
+__device__ void permute_small_body(const int32_t* ids, int T, int E, int K, int has_shared,
+                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                   int32_t* __restrict__ sorted_slot,
+                                   int32_t* __restrict__ slot_pos, int32_t* __restrict__ groups,
+                                   unsigned long long (*masks)[kMaxE], int* run, int* wsum,
+                                   bool init) {
   const int tid = threadIdx.x;
   const int TK = T * K, G = E + has_shared;
   // this thread's slot of the first chunk, loaded once (the whole input when
   // T*K <= 256), in flight during the LDS set-up
   const int id0 = tid < TK ? ids[tid] : -1;
-  for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
-  for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : 0;
-  __syncthreads();
+  if (init) {
+    for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
+    for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : 0;
+    __syncthreads();
+  }
   if (id0 >= 0 && id0 < E) atomicAdd(&run[id0], 1);
   for (int s = tid + kBlock; s < TK; s += kBlock) {
     const int e = ids[s];
@@ -154,6 +159,46 @@ __global__ __launch_bounds__(kBlock) void k_permute_small(
     scatter_chunk(c0 == 0 ? id0 : (s < TK ? ids[s] : -1), TK, E, c0, masks, run, sorted_slot, slot_pos);
   }
   if (has_shared) write_shared_group(T, TK, off_shared, sorted_slot, slot_pos, tid, kBlock);
+}
+
+__global__ __launch_bounds__(kBlock) void k_permute_small(
+    const int32_t* __restrict__ ids, int T, int E, int K, int has_shared,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
+    int32_t* __restrict__ groups) {
+  __shared__ unsigned long long masks[kBlock / 64][kMaxE];
+  __shared__ int run[kMaxE + 2];
+  __shared__ int wsum[kBlock / 64];
+  permute_small_body(ids, T, E, K, has_shared, counts, offsets, sorted_slot, slot_pos, groups,
+                     masks, run, wsum, true);
+}
+
+// Router top-K and permutation of a small batch in one block (T <=
+// kRouteFuseMaxT, one token per wave): wave t routes token t (the router
+// stage's rule, moe_topk.hpp) and keeps its ids in LDS as well, and the block
+// then permutes them.  Same outputs as the two kernels, one launch fewer.
+// (With more tokens than waves the routes of a wave run one after another,
+// and one route is a chain of ~4 us, so larger batches use the two kernels.)
+template <int MAXV>
+__global__ __launch_bounds__(kBlock) void k_route_permute_small(
+    const float* __restrict__ logits, int T, int E, int K, int has_shared,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ groups) {
+  __shared__ unsigned long long masks[kBlock / 64][kMaxE];
+  __shared__ int run[kMaxE + 2];
+  __shared__ int wsum[kBlock / 64];
+  __shared__ int32_t ids_l[kRouteFuseMaxT * 32];
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int G = E + has_shared;
+  for (int i = tid; i < (kBlock / 64) * kMaxE; i += kBlock) (&masks[0][0])[i] = 0ull;
+  for (int e = tid; e < G; e += kBlock) run[e] = (e == E) ? T : 0;
+  for (int t = wv; t < T; t += kBlock / 64)
+    route_row_topk<MAXV>(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K,
+                         ids_l + t * K);
+  __syncthreads();
+  permute_small_body(ids_l, T, E, K, has_shared, counts, offsets, sorted_slot, slot_pos, groups,
+                     masks, run, wsum, false);
 }
 
 // Tile histograms, written expert-major: cnt[e * ntiles + tile].
@@ -232,6 +277,11 @@ __global__ __launch_bounds__(kBlock) void k_permute_scatter(
 
 void register_permute_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_permute_small);
+  k.push_back((const void*)&k_route_permute_small<1>);
+  k.push_back((const void*)&k_route_permute_small<2>);
+  k.push_back((const void*)&k_route_permute_small<4>);
+  k.push_back((const void*)&k_route_permute_small<8>);
+  k.push_back((const void*)&k_route_permute_small<16>);
   k.push_back((const void*)&k_permute_count);
   k.push_back((const void*)&k_permute_scan_tiles);
   k.push_back((const void*)&k_permute_scatter);
@@ -261,6 +311,28 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int K, int has_share
   MOE_LAUNCH("permute_scan_tiles", s, k_permute_scan_tiles, dim3(E), dim3(kBlock), 0, s, cnt, nt, tot);
   MOE_LAUNCH("permute_scatter", s, k_permute_scatter, dim3(nt), dim3(kBlock), 0, s, ids, T, E, K,
              has_shared, nt, cnt, tot, counts, offsets, sorted_slot, slot_pos, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int K, int has_shared,
+                                int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups, void* ws,
+                                hipStream_t s) {
+  if (T > kRouteFuseMaxT) {
+    hipError_t e = launch_route_topk(logits, T, E, K, ids, w, s);
+    if (e != hipSuccess) return e;
+    return launch_permute(ids, T, E, K, has_shared, counts, offsets, sorted_slot, slot_pos,
+                          groups, ws, s);
+  }
+#define MOE_RP(MAXV)                                                                           \
+  MOE_LAUNCH("route_permute", s, (k_route_permute_small<MAXV>), dim3(1), dim3(kBlock), 0, s, \
+             logits, T, E, K, has_shared, ids, w, counts, offsets, sorted_slot, slot_pos, groups)
+  if (E <= 64) MOE_RP(1);
+  else if (E <= 128) MOE_RP(2);
+  else if (E <= 256) MOE_RP(4);
+  else if (E <= 512) MOE_RP(8);
+  else MOE_RP(16);
+#undef MOE_RP
   return hipGetLastError();
 }
 

@@ -46,10 +46,11 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 // Route one token: `row` holds its E logits (global or LDS memory).  Lane k
-// < K writes slot k of ids_t / w_t.  Every lane of the wave must call it.
+// < K writes slot k of ids_t / w_t (and of ids_copy when given, e.g. an LDS
+// copy for a consumer in the same block).  Every lane of the wave must call it.
 template <int MAXV>
 __device__ __forceinline__ void route_row_topk(const float* row, int E, int K, int32_t* ids_t,
-                                               float* w_t) {
+                                               float* w_t, int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x & 63;
   uint32_t key[MAXV], jx[MAXV];  // key and slot j (expert lane + 64 j) of each entry
 #pragma unroll
@@ -110,6 +111,7 @@ __device__ __forceinline__ void route_row_topk(const float* row, int E, int K, i
   if (lane < K) {
     ids_t[lane] = isel;
     w_t[lane] = ex / sum;
+    if (ids_copy) ids_copy[lane] = isel;
   }
 }
 

@@ -14,12 +14,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_PERMUTE, check
+from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_COMBINE,
+                   MOE_OP_PERMUTE, check)
 
 __all__ = [
     "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
     "moe_combine", "moe_layer", "workspace_bytes", "moe_expert_ffn_noalloc", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
-    "NVFP4Router", "moe_router_topk", "moe_combine_gated",
+    "NVFP4Router", "moe_router_topk", "moe_combine_gated", "moe_route_permute",
+    "moe_expert_ffn_combine",
 ]
 
 
@@ -173,6 +175,65 @@ def moe_permute(ids: torch.Tensor, E: int, has_shared: bool, ws: Optional[torch.
     return counts, offsets, sorted_slot, slot_pos, groups
 
 
+def moe_route_permute(logits: torch.Tensor, K: int, has_shared: bool,
+                      ws: Optional[torch.Tensor] = None, out=None):
+    """moe_route_topk + moe_permute (one kernel for small batches).
+    Returns (ids, w, counts, offsets, sorted_slot, slot_pos, groups)."""
+    _need(logits, torch.float32, name="logits")
+    T, E = logits.shape
+    G = E + int(has_shared)
+    S = T * K + (T if has_shared else 0)
+    dev = logits.device
+    i32 = torch.int32
+    if out is None:
+        out = (torch.empty((T, K), dtype=i32, device=dev),
+               torch.empty((T, K), dtype=torch.float32, device=dev),
+               torch.empty(G, dtype=i32, device=dev), torch.empty(G + 1, dtype=i32, device=dev),
+               torch.empty(S, dtype=i32, device=dev), torch.empty(S, dtype=i32, device=dev),
+               torch.empty(G + 1, dtype=i32, device=dev))
+    ids, w, counts, offsets, sorted_slot, slot_pos, groups = out
+    _need(ids, i32, (T, K), "ids")
+    _need(w, torch.float32, (T, K), "w")
+    nb = workspace_bytes(MOE_OP_PERMUTE, T, E, K, 0, 0, has_shared)
+    ws = _workspace(nb, dev, ws)
+    check(_lib.lib().moe_route_permute(_ptr(logits), T, E, K, int(has_shared), _ptr(ids), _ptr(w),
+                                       _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+                                       _ptr(slot_pos), _ptr(groups), _ptr(ws), nb, _stream()))
+    return ids, w, counts, offsets, sorted_slot, slot_pos, groups
+
+
+def moe_expert_ffn_combine(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tensor,
+                           sorted_slot: torch.Tensor, groups: torch.Tensor, w: torch.Tensor,
+                           slot_pos: torch.Tensor, act_mode: int = MOE_ACT_BF16,
+                           gate: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                           y_slots: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None):
+    """Expert FFN + combine (the combine folded into the down kernel for
+    decode batches).  Returns (y_slots, out)."""
+    _need(x, torch.bfloat16, name="x")
+    T, H = x.shape
+    if H != W.H:
+        raise ValueError("x width does not match the weight bank")
+    S = T * K + (T if W.has_shared else 0)
+    dev = x.device
+    y_slots = torch.empty((S, H), dtype=torch.bfloat16, device=dev) if y_slots is None else y_slots
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(y_slots, torch.bfloat16, (S, H), "y_slots")
+    _need(out, torch.bfloat16, (T, H), "out")
+    _need(w, torch.float32, (T, K), "w")
+    _need(slot_pos, torch.int32, (S,), "slot_pos")
+    if gate is not None:
+        _need(gate, torch.float32, (T,), "gate")
+    nb = workspace_bytes(MOE_OP_EXPERT_FFN_COMBINE, T, W.E, K, H, W.I, W.has_shared, act_mode)
+    ws = _workspace(nb, dev, ws)
+    st = W.struct()
+    check(_lib.lib().moe_expert_ffn_combine(ctypes.byref(st), _ptr(x), T, K, _ptr(offsets),
+                                            _ptr(sorted_slot), _ptr(groups), act_mode, _ptr(w),
+                                            _ptr(slot_pos), _ptr(gate), _ptr(y_slots), _ptr(out),
+                                            _ptr(ws), nb, _stream()))
+    return y_slots, out
+
+
 def moe_expert_ffn(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: torch.Tensor,
                    sorted_slot: torch.Tensor, groups: torch.Tensor, act_mode: int = MOE_ACT_BF16,
                    ws: Optional[torch.Tensor] = None, y_slots: Optional[torch.Tensor] = None,
@@ -250,8 +311,16 @@ def moe_combine_gated(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Te
 
 
 def moe_layer(W: NVFP4Weights, x: torch.Tensor, logits: torch.Tensor, K: int,
-              act_mode: int = MOE_ACT_BF16) -> dict:
-    """One layer call: route -> permute -> expert FFN -> combine, all on the GPU."""
+              act_mode: int = MOE_ACT_BF16, fused: bool = False) -> dict:
+    """One layer call: route -> permute -> expert FFN -> combine, all on the GPU.
+    fused=True uses moe_route_permute and moe_expert_ffn_combine (same results)."""
+    if fused:
+        ids, w, counts, offsets, sorted_slot, slot_pos, groups = moe_route_permute(
+            logits, K, W.has_shared)
+        y, out = moe_expert_ffn_combine(W, x, K, offsets, sorted_slot, groups, w, slot_pos,
+                                        act_mode)
+        return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,
+                    slot_pos=slot_pos, groups=groups, y_slots=y, out=out)
     ids, w = moe_route_topk(logits, K)
     counts, offsets, sorted_slot, slot_pos, groups = moe_permute(ids, W.E, W.has_shared)
     y = moe_expert_ffn(W, x, K, offsets, sorted_slot, groups, act_mode)

@@ -66,6 +66,7 @@ extern "C" {
 /* Operation ids of moe_workspace_bytes. */
 #define MOE_OP_PERMUTE 1
 #define MOE_OP_EXPERT_FFN 2
+#define MOE_OP_EXPERT_FFN_COMBINE 3
 
 /*
  * A bank of NVFP4 experts: E routed experts plus, if has_shared, one shared
@@ -199,6 +200,19 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_route_topk followed by moe_permute, with the same outputs (ids, w and
+ * the permutation arrays, bit for bit).  Batches of up to 4 tokens run as a
+ * single kernel: one block routes them (a wave per token) and permutes the
+ * ids from LDS, which takes a launch off the decode critical path; larger
+ * batches run the two stages' own kernels.  ws: as moe_permute
+ * (moe_workspace_bytes(MOE_OP_PERMUTE, ...)), NULL when that is 0.
+ */
+int moe_route_permute(const float* logits, int T, int E, int K, int has_shared, int32_t* ids,
+                      float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                      int32_t* slot_pos, int32_t* groups, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * Expert FFN of every group on the rows routed to it.  For the row of sorted
  * position p in group e (token t = sorted_slot[p] / K, or sorted_slot[p] - T*K
  * in the shared group):
@@ -235,6 +249,22 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
 int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
                    const int32_t* offsets, const int32_t* sorted_slot, const int32_t* groups,
                    int act_mode, uint16_t* y_slots, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn followed by the combine (moe_combine, or moe_combine_gated
+ * when `gate` is given) as one call, with the same y_slots and out.
+ *
+ *   w [T][K] float32, slot_pos [T*K + T*has_shared] int32   (in) routing
+ *   gate [T] float32 or NULL (needs has_shared)              (in) shared gate logit
+ *   y_slots, out                                            (out) as the two calls
+ *   ws  at least moe_workspace_bytes(MOE_OP_EXPERT_FFN_COMBINE, ...) bytes,
+ *       holding afterwards what moe_expert_ffn leaves in its workspace
+ */
+int moe_expert_ffn_combine(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
+                           const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* groups, int act_mode, const float* w,
+                           const int32_t* slot_pos, const float* gate, uint16_t* y_slots,
+                           uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

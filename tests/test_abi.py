@@ -19,7 +19,8 @@ def lib():
 def test_header_declares_the_four_layer_calls():
     names = declared_functions()
     for n in ("moe_route_topk", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_init",
-              "moe_last_error", "moe_workspace_bytes", "moe_router_topk", "moe_combine_gated"):
+              "moe_last_error", "moe_workspace_bytes", "moe_router_topk", "moe_combine_gated", "moe_route_permute",
+              "moe_expert_ffn_combine"):
         assert n in names
 
 
@@ -58,6 +59,22 @@ def test_argument_errors_are_reported_without_a_gpu(lib):
     cg = lib.moe_combine_gated
     assert cg(one, one, one, None, 4, 2, 16, one, None) == L.MOE_EINVAL       # no gate
     assert cg(one, one, one, one, 4, 2, 12, one, None) == L.MOE_EINVAL        # H % 8
+    rp = lib.moe_route_permute
+    assert rp(None, 4, 8, 2, 0, one, one, one, one, one, one, one, None, 0, None) == L.MOE_EINVAL
+    assert rp(one, 4, 8, 9, 0, one, one, one, one, one, one, one, None, 0, None) == L.MOE_EINVAL  # K > E
+    assert rp(one, 4096, 512, 10, 1, one, one, one, one, one, one, one, None, 0, None) == L.MOE_EWORKSPACE
+    fc = lib.moe_expert_ffn_combine
+    Ws = L.MoeNvfp4Weights(16, 16, 16, 16, 16, 8, 256, 128, 1)
+    assert fc(ctypes.byref(Ws), one, 4, 2, one, one, one, 0, None, one, None, one, one, one, 1 << 20,
+              None) == L.MOE_EINVAL                                                       # no w
+    assert fc(ctypes.byref(W), one, 4, 2, one, one, one, 0, one, one, one, one, one, one, 1 << 20,
+              None) == L.MOE_EINVAL                                                       # gate, no shared
+    assert fc(ctypes.byref(Ws), one, 4, 2, one, one, one, 5, one, one, None, one, one, one, 1 << 20,
+              None) == L.MOE_EUNSUPPORTED
+    need = lib.moe_workspace_bytes(L.MOE_OP_EXPERT_FFN_COMBINE, 4, 8, 2, 256, 128, 1, 0)
+    assert need >= lib.moe_workspace_bytes(L.MOE_OP_EXPERT_FFN, 4, 8, 2, 256, 128, 1, 0) > 0
+    assert fc(ctypes.byref(Ws), one, 4, 2, one, one, one, 0, one, one, None, one, one, one, need - 1,
+              None) == L.MOE_EWORKSPACE
     rt = lib.moe_router_topk
     R = L.MoeNvfp4Router(16, 16, 1.0, 64, 512, 1)
     assert rt(ctypes.byref(R), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL   # gate row, no gate

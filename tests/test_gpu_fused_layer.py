@@ -1,0 +1,148 @@
+"""GPU checks of the combined layer entry points: moe_route_permute (router
+top-K and permutation in one kernel for batches of up to 4 tokens, the two
+kernels above) and moe_expert_ffn_combine (FFN then combine in one call).
+Both must reproduce the separate calls bit for bit -- they run the same
+arithmetic in the same order -- and the layer through them must pass the same
+oracle gates as the unfused one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import bf16_np, flush, normwise, setup, x_dev
+from workloads import DECODE_TS, make_workload, workload_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    return setup()
+
+
+def _route_permute_both(moe, logits_np, K, E, has_shared):
+    lg = torch.from_numpy(logits_np).cuda()
+    fused = moe.moe_route_permute(lg, K, has_shared)
+    ids, w = moe.moe_route_topk(lg, K)
+    perm = moe.moe_permute(ids, E, has_shared)
+    torch.cuda.synchronize()
+    return fused, (ids, w) + tuple(perm)
+
+
+@pytest.mark.parametrize("E", [8, 100, 200, 512, 1000])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 16, 40])
+def test_route_permute_matches_the_two_calls(moe, E, T):
+    K = min(10, E)
+    for hs in (False, True):
+        wl = make_workload("rp", T=T, H=256, E=E, K=K, I=128, has_shared=hs, seed=T + E,
+                           with_weights=False)
+        fused, ref = _route_permute_both(moe, wl.logits, K, E, hs)
+        names = ("ids", "w", "counts", "offsets", "sorted_slot", "slot_pos", "groups")
+        for a, b, nm in zip(fused, ref, names):
+            assert torch.equal(a, b), f"{nm} E={E} T={T} shared={hs}"
+        # and the oracle's routing and permutation
+        ids_o, _ = oracle.route_topk(wl.logits, K)
+        assert np.array_equal(fused[0].cpu().numpy(), ids_o)
+        want = oracle.permute(ids_o, E, hs)
+        for g, w_, nm in zip(fused[2:6], want, names[2:6]):
+            assert np.array_equal(g.cpu().numpy(), w_), nm
+
+
+def test_route_permute_ties_and_nan(moe):
+    T, E, K = 4, 64, 6
+    lg = np.zeros((T, E), dtype=np.float32)
+    lg[0, 10:20] = 1.0
+    lg[1, 5] = np.nan
+    lg[2, :] = -np.inf
+    lg[3, ::2] = np.inf
+    fused, ref = _route_permute_both(moe, lg, K, E, True)
+    for a, b in zip(fused, ref):
+        assert torch.equal(a, b)
+    ids_o, _ = oracle.route_topk(lg, K)
+    assert np.array_equal(fused[0].cpu().numpy(), ids_o)
+
+
+def _ffn_combine_both(moe, wl, act_mode=0, gate=None, repeats=2):
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    x = x_dev(wl.x_bf16)
+    ids, w, counts, offsets, sorted_slot, slot_pos, groups = moe.moe_route_permute(
+        torch.from_numpy(wl.logits).cuda(), wl.K, wl.has_shared)
+    y_ref = moe.moe_expert_ffn(W, x, wl.K, offsets, sorted_slot, groups, act_mode)
+    out_ref = (moe.moe_combine(y_ref, w, slot_pos, wl.K, wl.has_shared) if gate is None
+               else moe.moe_combine_gated(y_ref, w, slot_pos, gate, wl.K))
+    ws = None
+    outs = []
+    for _ in range(repeats):  # repeated calls give the same bits
+        y, out = moe.moe_expert_ffn_combine(W, x, wl.K, offsets, sorted_slot, groups, w, slot_pos,
+                                            act_mode, gate=gate, ws=ws)
+        outs.append((y.clone(), out.clone()))
+    torch.cuda.synchronize()
+    for y, out in outs:
+        assert torch.equal(y, y_ref)
+        assert torch.equal(out, out_ref)
+    return outs[0][1], w, slot_pos
+
+
+@pytest.mark.parametrize("T", DECODE_TS)
+def test_ffn_combine_decode_full_size(moe, T):
+    wl = workload_for("decode", T=T)
+    flush(f"ffn_combine decode T={T}")
+    out, w, slot_pos = _ffn_combine_both(moe, wl)
+    # the fused layer against the exact oracle, with the unfused layer's gate
+    exact = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
+    assert normwise(bf16_np(out), exact["out"]) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=5, H=2048, E=64, K=10, I=512, has_shared=True),
+    dict(T=8, H=256, E=4, K=2, I=128, has_shared=True),      # smallest H and I
+    dict(T=7, H=4096, E=16, K=4, I=1024, has_shared=False),  # largest H and I
+    dict(T=3, H=512, E=16, K=4, I=256, has_shared=False),
+    dict(T=300, H=512, E=16, K=4, I=256, has_shared=True),   # the unfused (prefill) branch
+])
+def test_ffn_combine_shapes(moe, cfg):
+    wl = make_workload("fc", seed=11, **cfg)
+    flush(f"ffn_combine {cfg}")
+    _ffn_combine_both(moe, wl)
+
+
+def test_ffn_combine_fp8_and_gate(moe):
+    wl = workload_for("decode", T=8)
+    g = torch.from_numpy(np.linspace(-3, 3, wl.T).astype(np.float32)).cuda()
+    _ffn_combine_both(moe, wl, act_mode=1)
+    _ffn_combine_both(moe, wl, gate=g)
+    _ffn_combine_both(moe, wl, act_mode=1, gate=g)
+
+
+def test_ffn_combine_no_active_group(moe):
+    """Every id out of range and no shared expert: no group is active, and
+    the combine still writes the (all-zero) output."""
+    wl = make_workload("na", T=4, H=512, E=16, K=4, I=256, has_shared=False, seed=3)
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    x = x_dev(wl.x_bf16)
+    ids = torch.full((wl.T, wl.K), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((wl.T, wl.K), 0.25, dtype=torch.float32, device="cuda")
+    counts, offsets, sorted_slot, slot_pos, groups = moe.moe_permute(ids, wl.E, False)
+    out0 = torch.full((wl.T, wl.H), 7.0, dtype=torch.bfloat16, device="cuda")
+    _, out = moe.moe_expert_ffn_combine(W, x, wl.K, offsets, sorted_slot, groups, w, slot_pos,
+                                        out=out0)
+    torch.cuda.synchronize()
+    assert int(groups[0].item()) == 0
+    assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("T", DECODE_TS)
+def test_fused_layer_against_oracle(moe, T):
+    """moe_layer(fused=True) through the same gates as the unfused layer."""
+    wl = workload_for("decode", T=T)
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    r = moe.moe_layer(W, x_dev(wl.x_bf16), torch.from_numpy(wl.logits).cuda(), wl.K, fused=True)
+    torch.cuda.synchronize()
+    exact = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
+    emul = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K, h_round="bf16",
+                            y_round="bf16")
+    assert np.array_equal(r["ids"].cpu().numpy(), exact["ids"])
+    assert np.array_equal(r["sorted_slot"].cpu().numpy(), exact["sorted_slot"])
+    out = bf16_np(r["out"])
+    assert normwise(out, emul["out"]) <= 8e-3
+    assert normwise(out, exact["out"]) <= 2e-2
