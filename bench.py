@@ -47,7 +47,7 @@ NLOGITS = 16
 # rocprofv3 counter summary of the expert-FFN kernels (FETCH_SIZE + WRITE_SIZE
 # per dispatch, calibrated against a 1 GiB copy), with the hash of the decode
 # kernel sources it was measured on.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_ffn_hbm_traffic_decode_T8_prefill_T4096.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_ffn_hbm_traffic_all_workloads.md")
 DECODE_SOURCES = ["bit_block_quantized_nvfp4_amd/csrc/moe_ffn_decode.hip",
                   "bit_block_quantized_nvfp4_amd/csrc/moe_ffn_common.hpp",
                   "bit_block_quantized_nvfp4_amd/csrc/moe_device.hpp"]
@@ -169,8 +169,14 @@ def time_steps(runner, torch, steps, warmup, graph=True):
 
 
 def kernel_times(runner, torch, moe_ops, steps, warmup):
+    """Per-kernel durations from the HIP events the library records around each
+    launch.  A short GPU spin goes first, so the whole pass is queued before
+    the GPU reaches it and each event pair brackets GPU work only (not the
+    host's time between recording the start event and launching the kernel)."""
+    torch.cuda.synchronize()
     moe_ops.timing_reset()
     moe_ops.timing_enable(True)
+    torch.cuda._sleep(int(2e7))      # ~10 ms of spinning while the host enqueues the pass
     for i in range(steps):
         runner.run(warmup + i)
     torch.cuda.synchronize()
@@ -287,13 +293,17 @@ def counter_pass(moe, torch, banks, base, steps):
     act = r.active_groups()
     print(f"# counter pass: decode T=8, {steps} layer calls, active groups per logits set {act}",
           file=sys.stderr, flush=True)
-    wl = workload_for("prefill", with_weights=False)
-    wl.weights = base.weights
-    r = LayerRunner(moe, torch, banks, wl, [wl.logits])
-    for i in range(3):
-        r.run(i)
-    torch.cuda.synchronize()
-    print("# counter pass: prefill T=4096, 3 layer calls", file=sys.stderr, flush=True)
+    for name, act_mode, calls in (("prefill", 0, 3), ("long_prefill", 0, 1), ("fp8_arm", 1, 1)):
+        wl = workload_for(name, with_weights=False)
+        wl.weights = base.weights
+        r = LayerRunner(moe, torch, banks, wl, [wl.logits], act_mode=act_mode)
+        for i in range(calls):
+            r.run(i)
+        torch.cuda.synchronize()
+        print(f"# counter pass: {name} T={wl.T} act_mode={act_mode}, {calls} layer call(s)",
+              file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -311,8 +321,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--counter-pass", action="store_true",
-                    help="eager launches only, for rocprofv3 --pmc: the T=8 decode layer, the T=4096 "
-                         "prefill layer and a plain copy of COPY_BYTES (the counters' scale reference)")
+                    help="eager launches only, for rocprofv3 --pmc: the T=8 decode layer, the T=4096, "
+                         "T=32768 and FP8 T=8192 layers and a plain copy of COPY_BYTES (the counters' "
+                         "scale reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
