@@ -98,7 +98,11 @@ typedef struct moe_nvfp4_weights {
  * Check that the current HIP device is gfx950 and that every kernel of the
  * library is loadable (resolved once here, never per launch).  Returns MOE_OK,
  * MOE_EUNSUPPORTED (other architecture, the message names it) or MOE_EHIP.
- * The other entry points call it implicitly on first use per device.
+ * The other entry points call it implicitly on first use per device.  The
+ * refusing gate is the pages' convention for a single-architecture pilot: the
+ * loader of the issue "EXL3 Qwen3.8-Flash-Next on CUDA sm_120 ...", section
+ * "Scope: a pilot on sm_120", refuses any other compute capability with a
+ * message that names the gate; here the gate is gfx950.
  */
 int moe_init(void);
 
@@ -113,7 +117,9 @@ size_t moe_workspace_bytes(int op, int T, int E, int K, int H, int I, int has_sh
                            int act_mode);
 
 /*
- * Router top-K: for each token t, rank the E experts by logit (larger first,
+ * Router top-K (the top-k of the router stage, the first prefill op of the
+ * issue above's list; rank rule of the page "handover briefs", item A1 and the
+ * indexer-selection kernel spec): for each token t, rank the E experts by logit (larger first,
  * equal logits -> lower index first, NaN counts as -inf), put the rank-k
  * expert in slot k, and weight the K selected experts by the softmax of their
  * logits: w[t][k] = exp(z_k - z_0) / sum_j exp(z_j - z_0), where a term with
@@ -174,7 +180,11 @@ int moe_router_topk(const moe_nvfp4_router* R, const uint16_t* x, int T, int K, 
                     float* w, float* logits, float* gate, void* stream);
 
 /*
- * Group the T*K routed slots (slot s = t*K + k) by expert.
+ * Group the T*K routed slots (slot s = t*K + k) by expert: the token
+ * permutation, one of the per-layer MoE tensors that the prefill issue ("[job]
+ * Qwen3.8-Flash-Next: long-context cold prefill to SGLang parity", section
+ * "Localising the remaining ~0.56 %", the per-layer dump list) names between
+ * the router's top-k ids/weights and the routed outputs before the combine.
  *
  *   ids         [T][K] int32, each in [0, E)   (in)
  *   counts      [E'] int32        (out) slots per group; counts[E] = T if shared

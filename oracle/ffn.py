@@ -20,7 +20,9 @@ Definitions:
 Options for diagnostics only: ``h_round``/``y_round`` = "bf16" round the
 intermediate h or the per-slot outputs to bf16 (via torch's fp32 -> bf16 cast,
 after an fp64 -> fp32 step) to mirror where the GPU stores bf16; ``act_mode`` =
-"fp8_row" feeds the gate_up GEMM with the per-row e4m3-quantised activations.
+"fp8_row" feeds the gate_up GEMM with the per-row e4m3-quantised activations,
+"fp8_routed" / "fp8_shared" only those of the routed / the shared expert
+(activation_arms).
 
 Pins: pure-Python math.fsum loops on the tiny layer; ``bf16_bits_to_f64``
 against the bf16 closed form on all 65,536 patterns and hand-worked patterns,
@@ -81,11 +83,12 @@ def expert_ffn(rows: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
 
 
 def expert_outputs(xin: np.ndarray, bank, T: int, K: int, offsets, sorted_slot,
-                   h_round: str = "none", groups=None) -> np.ndarray:
+                   h_round: str = "none", groups=None, xin_shared=None) -> np.ndarray:
     """Per-slot expert outputs in sorted order: y [T*K (+T), H] float64.
 
     ``groups`` optionally restricts the work to some group indices (the other
-    rows stay NaN), for sampled checks at full size.
+    rows stay NaN), for sampled checks at full size.  ``xin_shared``, when
+    given, is the activation the shared expert (group E) reads instead of xin.
     """
     n_groups = len(offsets) - 1
     y = np.full((int(offsets[-1]), bank.H), np.nan, dtype=np.float64)
@@ -96,8 +99,27 @@ def expert_outputs(xin: np.ndarray, bank, T: int, K: int, offsets, sorted_slot,
         slots = np.asarray(sorted_slot[a:b], dtype=np.int64)
         toks = np.where(slots < T * K, slots // K, slots - T * K)
         wg, wu, wd = dequant_expert(bank, e)
-        y[a:b] = expert_ffn(xin[toks], wg, wu, wd, h_round)
+        src = xin_shared if (xin_shared is not None and bank.has_shared and e == bank.E) else xin
+        y[a:b] = expert_ffn(src[toks], wg, wu, wd, h_round)
     return y
+
+
+def activation_arms(x: np.ndarray, act_mode: str):
+    """(activations of the routed experts, of the shared expert) for an arm:
+    "bf16" both exact; "fp8_row" both per-row e4m3 ([attr] option (a), the
+    pages' arm E quantises routed and shared); "fp8_routed" routed e4m3 and
+    the shared expert exact (the shared-expert A/B table's arm S, the shared
+    expert on bf16); "fp8_shared" the mirror (routed exact, shared e4m3)."""
+    if act_mode == "bf16":
+        return x, x
+    q = rowquant_dequant(x.astype(np.float32))
+    if act_mode == "fp8_row":
+        return q, q
+    if act_mode == "fp8_routed":
+        return q, x
+    if act_mode == "fp8_shared":
+        return x, q
+    raise ValueError(act_mode)
 
 
 def combine(y_slots: np.ndarray, w: np.ndarray, slot_pos: np.ndarray, T: int, K: int,
@@ -126,13 +148,8 @@ def moe_layer(x_bits: np.ndarray, logits: np.ndarray, bank, K: int, act_mode: st
     x = bf16_bits_to_f64(x_bits)
     ids, w = route_topk(logits, K)
     counts, offsets, sorted_slot, slot_pos = permute(ids, bank.E, bank.has_shared)
-    if act_mode == "bf16":
-        xin = x
-    elif act_mode == "fp8_row":
-        xin = rowquant_dequant(x.astype(np.float32))
-    else:
-        raise ValueError(act_mode)
-    y = expert_outputs(xin, bank, T, K, offsets, sorted_slot, h_round)
+    xin, xin_sh = activation_arms(x, act_mode)
+    y = expert_outputs(xin, bank, T, K, offsets, sorted_slot, h_round, xin_shared=xin_sh)
     yc = _round_bf16(y) if y_round == "bf16" else y
     out = combine(yc, w, slot_pos, T, K, bank.has_shared)
     return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,

@@ -199,3 +199,29 @@ def test_fp8_arm_emulation_within_the_gate_on_heavy_tails():
     fp8 = oracle.moe_layer(w.x_bf16, w.logits, w.weights, w.K, act_mode="fp8_row")["out"]
     err = np.max(np.abs(fp8 - exact)) / np.max(np.abs(exact))
     assert 0 < err < 6e-2
+
+
+def test_activation_arms_per_expert_class():
+    """The per-class arms (the shared-expert A/B table's arm S and its
+    mirror): routed slots carry exactly the outputs of the arm their class
+    uses, shared slots those of the other, and without a shared expert
+    "fp8_routed" is "fp8_row" and "fp8_shared" is "bf16"."""
+    w = make_workload("arms", T=6, H=256, E=8, K=2, I=128, has_shared=True, seed=4)
+    lay = {m: oracle.moe_layer(w.x_bf16, w.logits, w.weights, w.K, act_mode=m)
+           for m in ("bf16", "fp8_row", "fp8_routed", "fp8_shared")}
+    TK = w.T * w.K
+    pos = lay["bf16"]["slot_pos"]
+    routed, shared = pos[:TK], pos[TK:]
+    for m, r_src, s_src in (("fp8_routed", "fp8_row", "bf16"), ("fp8_shared", "bf16", "fp8_row")):
+        y = lay[m]["y_slots"]
+        assert np.array_equal(y[routed], lay[r_src]["y_slots"][routed])
+        assert np.array_equal(y[shared], lay[s_src]["y_slots"][shared])
+        # the combine is linear in the shared rows
+        want = lay[r_src]["out"] - lay[r_src]["y_slots"][shared] + lay[s_src]["y_slots"][shared]
+        assert np.allclose(lay[m]["out"], want, rtol=0, atol=1e-12 * np.abs(want).max())
+    assert not np.array_equal(lay["fp8_routed"]["out"], lay["fp8_row"]["out"])
+    w0 = make_workload("arms0", T=6, H=256, E=8, K=2, I=128, has_shared=False, seed=4)
+    o = {m: oracle.moe_layer(w0.x_bf16, w0.logits, w0.weights, w0.K, act_mode=m)["out"]
+         for m in ("bf16", "fp8_row", "fp8_routed", "fp8_shared")}
+    assert np.array_equal(o["fp8_routed"], o["fp8_row"])
+    assert np.array_equal(o["fp8_shared"], o["bf16"])
