@@ -224,8 +224,8 @@ def cpu_baseline_sampled(wl, act_mode=0, budget_s=8.0):
     counts, offsets, sorted_slot, slot_pos = oracle.permute(ids, E, wl.has_shared)
     t_rp = time.perf_counter() - t0
     x = oracle.ffn.bf16_bits_to_f64(wl.x_bf16)
-    if act_mode:
-        x = oracle.rowquant_dequant(x.astype(np.float32))
+    x_routed, x_shared = oracle.ffn.activation_arms(
+        x, {0: "bf16", 1: "fp8_row", 2: "fp8_routed", 3: "fp8_shared"}[act_mode])
     active = [g for g in range(len(counts)) if counts[g] > 0]
     rng = np.random.default_rng(0)
     order = ([E] if wl.has_shared else []) + [int(g) for g in rng.permutation(
@@ -239,7 +239,7 @@ def cpu_baseline_sampled(wl, act_mode=0, budget_s=8.0):
         t1 = time.perf_counter()
         wg, wu, wd = oracle.ffn.dequant_expert(wl.weights, g)
         t2 = time.perf_counter()
-        oracle.expert_ffn(x[toks], wg, wu, wd)
+        oracle.expert_ffn((x_shared if g == E else x_routed)[toks], wg, wu, wd)
         t3 = time.perf_counter()
         t_dq.append(t2 - t1)
         t_ffn += t3 - t2
@@ -410,7 +410,7 @@ def main():
                 "kernels": {k: round(v["avg_us"], 2) for k, v in d["kernels"].items()}}
             print(f"# decode T={T}: {d['ms_per_step'] * 1e3:.1f} us/layer", file=sys.stderr, flush=True)
         for name, act_mode in (("prefill", 0), ("long_prefill", 0), ("fp8_arm", 1),
-                               ("fp8_arm", 0)):
+                               ("fp8_arm", 0), ("fp8_arm", 2)):
             wl = workload_for(name, with_weights=False)
             wl.weights = base.weights
             lsets = [workload_for(name, seed=s, with_weights=False).logits for s in range(2)]
@@ -420,9 +420,11 @@ def main():
             S = wl.T * wl.K + wl.T
             fl_gu = 2.0 * S * H * 2 * I
             fl_dn = 2.0 * S * I * H
-            key = f"{name}_T{wl.T}" + ("_fp8" if act_mode else ("_bf16" if name == "fp8_arm" else ""))
-            ent = {"workload": WORKLOAD_TEXT[name] + (", FP8 row-quantised activations"
-                                                      if act_mode else ""),
+            suffix = {0: "_bf16" if name == "fp8_arm" else "", 1: "_fp8", 2: "_fp8_routed"}[act_mode]
+            key = f"{name}_T{wl.T}" + suffix
+            ent = {"workload": WORKLOAD_TEXT[name] + {0: "", 1: ", FP8 row-quantised activations",
+                                                      2: ", FP8 activations for the routed experts, "
+                                                         "bf16 for the shared expert"}[act_mode],
                    "tokens_per_s": round(wl.T / (ms / 1e3), 1), "us_per_layer": round(ms * 1e3, 1),
                    "layer_TFLOPs": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12, 1),
                    "layer_frac": round((fl_gu + fl_dn) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -441,7 +443,10 @@ def main():
                 r.run(0)
                 torch.cuda.synchronize()
                 outs[act_mode] = r.out.float().clone()
-                if 0 in outs and 1 in outs:
+                if 0 in outs and act_mode != 0:
+                    d = (outs[act_mode] - outs[0]).abs().max() / outs[0].abs().max()
+                    ent["vs_bf16_path_normwise"] = round(float(d), 5)
+                if act_mode == 0 and 1 in outs:
                     d = (outs[1] - outs[0]).abs().max() / outs[0].abs().max()
                     extra["fp8_arm_T8192_fp8"]["vs_bf16_path_normwise"] = round(float(d), 5)
             if not args.no_cpu:

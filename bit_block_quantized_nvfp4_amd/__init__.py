@@ -5,7 +5,9 @@ The compute path is the HIP library ``libmoe_nvfp4.so`` (C ABI in
 """
 from .ops import (  # noqa: F401
     MOE_ACT_BF16,
+    MOE_ACT_FP8_ROUTED,
     MOE_ACT_FP8_ROW,
+    MOE_ACT_FP8_SHARED,
     NVFP4Router,
     NVFP4Weights,
     moe_combine,

@@ -18,6 +18,8 @@ MOE_EHIP = -3
 MOE_EWORKSPACE = -4
 MOE_ACT_BF16 = 0
 MOE_ACT_FP8_ROW = 1
+MOE_ACT_FP8_ROUTED = 2
+MOE_ACT_FP8_SHARED = 3
 MOE_OP_PERMUTE = 1
 MOE_OP_EXPERT_FFN = 2
 MOE_OP_EXPERT_FFN_COMBINE = 3

@@ -173,7 +173,7 @@ size_t moe_workspace_bytes(int op, int T, int E, int K, int H, int I, int has_sh
   if (!sizes_ok_common(T, E, K) || (has_shared != 0 && has_shared != 1)) return 0;
   if (op == MOE_OP_PERMUTE) return moe::permute_workspace_bytes(T, E, K);
   if (op == MOE_OP_EXPERT_FFN || op == MOE_OP_EXPERT_FFN_COMBINE) {
-    if (H <= 0 || I <= 0 || (act_mode != MOE_ACT_BF16 && act_mode != MOE_ACT_FP8_ROW)) return 0;
+    if (H <= 0 || I <= 0 || act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED) return 0;
     return op == MOE_OP_EXPERT_FFN ? moe::ffn_workspace_bytes(T, K, H, I, has_shared, act_mode)
                                    : moe::ffn_combine_workspace_bytes(T, K, H, I, has_shared, act_mode);
   }
@@ -215,7 +215,7 @@ int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
     return fail(MOE_EINVAL, "moe_expert_ffn: null pointer");
   if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
     return fail(MOE_EINVAL, "moe_expert_ffn: null weight pointer");
-  if (act_mode != MOE_ACT_BF16 && act_mode != MOE_ACT_FP8_ROW)
+  if (act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED)
     return fail(MOE_EUNSUPPORTED, "moe_expert_ffn: unknown act_mode %d", act_mode);
   if (!sizes_ok_common(T, W->E, K) || (W->has_shared != 0 && W->has_shared != 1))
     return fail(MOE_EINVAL, "moe_expert_ffn: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
@@ -239,7 +239,7 @@ int moe_expert_ffn_noalloc(const moe_nvfp4_weights* W, const uint16_t* x, int T,
     return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: null pointer");
   if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
     return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: null weight pointer");
-  if (act_mode != MOE_ACT_BF16 && act_mode != MOE_ACT_FP8_ROW)
+  if (act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED)
     return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_noalloc: unknown act_mode %d", act_mode);
   if (!sizes_ok_common(T, W->E, K) || (W->has_shared != 0 && W->has_shared != 1))
     return fail(MOE_EINVAL, "moe_expert_ffn_noalloc: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
@@ -288,7 +288,7 @@ int moe_expert_ffn_combine(const moe_nvfp4_weights* W, const uint16_t* x, int T,
     return fail(MOE_EINVAL, "moe_expert_ffn_combine: null pointer");
   if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
     return fail(MOE_EINVAL, "moe_expert_ffn_combine: null weight pointer");
-  if (act_mode != MOE_ACT_BF16 && act_mode != MOE_ACT_FP8_ROW)
+  if (act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED)
     return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_combine: unknown act_mode %d", act_mode);
   if (!sizes_ok_common(T, W->E, K) || (W->has_shared != 0 && W->has_shared != 1))
     return fail(MOE_EINVAL, "moe_expert_ffn_combine: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");

@@ -36,11 +36,17 @@ void register_ffn_kernels(std::vector<const void*>& k) {
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Per-class arms: the routed and the shared expert read different activation
+// forms, kept as one [2T][H] array (rows T.. for the shared group).
+static inline bool mixed_arm(int act_mode) {
+  return act_mode == MOE_ACT_FP8_ROUTED || act_mode == MOE_ACT_FP8_SHARED;
+}
+
 size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_mode) {
   const size_t S = (size_t)T * K + (has_shared ? (size_t)T : 0);
   size_t b = align256(S * I * sizeof(uint16_t));
-  if (act_mode == MOE_ACT_FP8_ROW) b += align256((size_t)T * H) + align256((size_t)T * sizeof(float));
-  return b + xprep_workspace_bytes(T, H);
+  if (act_mode != MOE_ACT_BF16) b += align256((size_t)T * H) + align256((size_t)T * sizeof(float));
+  return b + xprep_workspace_bytes(mixed_arm(act_mode) ? 2 * T : T, H);
 }
 
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
@@ -54,22 +60,32 @@ hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   wp += align256(S * I * sizeof(uint16_t));
   uint8_t* xq = nullptr;
   float* xs = nullptr;
-  const bool fp8 = act_mode == MOE_ACT_FP8_ROW;
-  if (fp8) {
+  if (act_mode != MOE_ACT_BF16) {
     xq = wp;
     wp += align256((size_t)T * H);
     xs = (float*)wp;
     wp += align256((size_t)T * sizeof(float));
   }
   if (T <= kDecodeMaxT && decode_supported(H, I))
-    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, fp8, hbuf, xq, xs, y, s);
+    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, act_mode, hbuf, xq, xs, y, s);
+  const bool mixed = mixed_arm(act_mode);
+  const int rows = mixed ? 2 * T : T;
   _Float16* xh = (_Float16*)wp;
-  float* rowfac = (float*)(wp + align256((size_t)T * H * sizeof(_Float16)));
-  hipError_t e = launch_xprep(x, T, H, fp8, xh, rowfac, xq, xs, s);
+  float* rowfac = (float*)(wp + align256((size_t)rows * H * sizeof(_Float16)));
+  hipError_t e;
+  if (!mixed) {
+    e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_ROW, xh, rowfac, xq, xs, s);
+  } else {  // rows [0, T): the routed experts' form; rows [T, 2T): the shared expert's
+    e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_ROUTED, xh, rowfac, xq, xs, s);
+    if (e == hipSuccess)
+      e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_SHARED, xh + (size_t)T * H, rowfac + T,
+                       xq, xs, s);
+  }
   if (e != hipSuccess) return e;
-  if (fused_supported(T, H, I))
-    return launch_prefill_fused(W, T, K, offsets, sorted_slot, xh, rowfac, hbuf, y, s);
-  return launch_prefill_ffn(W, T, K, offsets, sorted_slot, xh, rowfac, hbuf, y, s);
+  const int shared_rows = mixed ? T : 0;
+  if (fused_supported(rows, H, I))
+    return launch_prefill_fused(W, T, K, offsets, sorted_slot, xh, rowfac, shared_rows, hbuf, y, s);
+  return launch_prefill_ffn(W, T, K, offsets, sorted_slot, xh, rowfac, shared_rows, hbuf, y, s);
 }
 
 // The expert FFN followed by the combine kernel, as one call.  (Folding the

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* __restrict__ scale2, const uint16_t* __restrict__ x,
     uint8_t* __restrict__ xq, float* __restrict__ xs, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ groups, int T, int K,
-    int H, int I, int has_shared, uint16_t* __restrict__ h) {
+    int H, int I, int has_shared, int fp8_sel, int shared_g, uint16_t* __restrict__ h) {
   extern __shared__ __align__(16) _Float16 xl[];
   constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
   constexpr int NDMA = (TR * CPR + 64 * WPB - 1) / (64 * WPB);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // k_dec_xprep, bit for bit): wave wv converts rows wv, wv + WPB, ...; the
   // row's epilogue factor goes to fac[]; with FP8, block 0 also writes the
   // row codes and scales to xq / xs.
-  auto convert_rows = [&]() {
+  auto convert_rows = [&](bool fp8_row) {
     constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
     for (int r = wv; r < TR; r += WPB) {
       float amax = 0.f;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       }
       amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
       float mul, rf;
-      if (FP8) {
+      if (fp8_row) {
         rf = amax > 0.f ? amax / 448.0f : 1.0f;
         mul = amax > 0.f ? 448.0f / amax : 1.0f;
       } else {
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
         mul = ldexpf(1.0f, sh);
         rf = ldexpf(1.0f, -sh);
       }
-      const bool wr = FP8 && blockIdx.x == 0 && r < T;
+      const bool wr = fp8_row && fp8_sel == 0 && blockIdx.x == 0 && r < T;
       if (lane == 0) {
         fac[r] = rf;
         if (wr) xs[r] = rf;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
         uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
         const u32x4 v = vr[k];
         u32x4 o;
-        if (FP8) {
+        if (fp8_row) {
           u32x2 code;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -332,9 +332,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   asm volatile("" ::"s"(e));  // (keeps the second lookup above the branch)
   if (a >= nact) {            // uniform per block: nothing to do, but the DMA into
     wait_vmcnt<0>();          // this block's LDS must land before the block ends
-    if (FP8 && blockIdx.x == 0) {  // the row codes and scales are outputs of the call
-      __builtin_amdgcn_s_barrier();  // even when no group is active
-      convert_rows();
+    if (FP8 && fp8_sel == 0 && blockIdx.x == 0) {  // the row codes and scales are outputs
+      __builtin_amdgcn_s_barrier();  // of the call even when no group is active
+      convert_rows(true);
     }
     return;
   }
@@ -386,7 +386,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // (5) activation rows -> f16 in place (LDS only).  Two passes over each row
   // in LDS (absmax, then convert), one row at a time; each pass issues all of
   // the lane's chunks of the row at once, and the absmax reduction is DPP-only.
-  convert_rows();
+  // the arm of this block's group: every group (fp8_sel 0), only the routed
+  // groups (1) or only the shared group (2) read e4m3 rows
+  const bool shared_grp = e == shared_g;  // shared_g = E with a shared expert, else -1
+  convert_rows(FP8 && (fp8_sel == 0 || (fp8_sel == 1) != shared_grp));
   // the scale runs and the slot have landed once only the code loads are
   // outstanding; LDS traffic done, then the barrier publishes the rows.
   wait_vmcnt<2 * D>();
@@ -692,15 +695,18 @@ size_t xprep_workspace_bytes(int T, int H) {
 template <int NCH, int WPB>
 static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                                const int32_t* offsets, const int32_t* sorted_slot,
-                               const int32_t* groups, bool fp8, uint8_t* xq, float* xs,
+                               const int32_t* groups, int act_mode, uint8_t* xq, float* xs,
                                uint16_t* hbuf, dim3 grid, hipStream_t s) {
+  const bool fp8 = act_mode != MOE_ACT_BF16;
+  const int fp8_sel = act_mode == MOE_ACT_FP8_ROUTED ? 1 : (act_mode == MOE_ACT_FP8_SHARED ? 2 : 0);
+  const int shared_g = W.has_shared ? W.E : -1;
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
   const size_t lds = (size_t)tr * H * 2 + 256 + (size_t)WPB * 2 * 16 * (H / 16);
 #define MOE_DEC_GU1(TR, F8)                                                                       \
   MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR, F8>), grid, dim3(64 * WPB), lds, s,  \
              W.gu_codes, W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, groups, T, K, H, \
-             I, hs, hbuf)
+             I, hs, fp8_sel, shared_g, hbuf)
 #define MOE_DEC_GU2(TR)                \
   do {                                 \
     if (fp8) MOE_DEC_GU1(TR, true);    \
@@ -716,7 +722,7 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
 
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
-                             const int32_t* groups, bool fp8, uint16_t* hbuf, uint8_t* xq,
+                             const int32_t* groups, int act_mode, uint16_t* hbuf, uint8_t* xq,
                              float* xs, uint16_t* y, hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
@@ -735,9 +741,9 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
 #define MOE_DEC_GU(NCH)                                                                          \
   do {                                                                                           \
     if (wpb_g == 4)                                                                              \
-      launch_dec_gate_up<NCH, 4>(W, x, T, K, offsets, sorted_slot, groups, fp8, xq, xs, hbuf, g1, s); \
+      launch_dec_gate_up<NCH, 4>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, hbuf, g1, s); \
     else                                                                                         \
-      launch_dec_gate_up<NCH, 1>(W, x, T, K, offsets, sorted_slot, groups, fp8, xq, xs, hbuf, g1, s); \
+      launch_dec_gate_up<NCH, 1>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, hbuf, g1, s); \
   } while (0)
   if (nch == 2) MOE_DEC_GU(2);
   else if (nch == 4) MOE_DEC_GU(4);

@@ -385,18 +385,21 @@ __global__ __launch_bounds__(64 * kFNW, 1) void k_prefill_ffn(
     const float* __restrict__ scale2, const _Float16* __restrict__ xh,
     const float* __restrict__ rowfac, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, int T, int K, int H, int I, int G, int has_shared,
-    uint16_t* __restrict__ h, uint16_t* __restrict__ y) {
+    int shared_rows, uint16_t* __restrict__ h, uint16_t* __restrict__ y) {
   constexpr int NTHR = 64 * kFNW;
   __shared__ __align__(16) FfnSmem sm;
-  const uint32_t xbytes = (uint32_t)T * (uint32_t)H * 2u;  // < 2^31 (fused_supported)
+  // activation rows [T + shared_rows][H]: the shared group reads rows
+  // shared_rows + t (its own activation arm) when shared_rows > 0
+  const uint32_t xbytes = (uint32_t)(T + shared_rows) * (uint32_t)H * 2u;  // < 2^31 (fused_supported)
   PfTile ti;
   if (!pf_find_tile<NTHR>(offsets, G, 1, sm.base, sm.wsum, &ti)) return;
+  const int roff = (has_shared && ti.g == G - 1) ? shared_rows : 0;
   for (int r = threadIdx.x; r < kPM; r += NTHR) {
     int tk = -1;
     if (r < ti.rows) tk = slot_token(sorted_slot[ti.p0 + r], T, K, has_shared);
     sm.row_ok[r] = tk >= 0;
-    sm.rowoff[r] = tk >= 0 ? (uint32_t)tk * (uint32_t)H * 2u : 0u;  // token 0's row for padding rows
-    sm.row_fac[r] = tk >= 0 ? rowfac[tk] : 0.f;
+    sm.rowoff[r] = tk >= 0 ? (uint32_t)(tk + roff) * (uint32_t)H * 2u : 0u;  // row 0 for padding rows
+    sm.row_fac[r] = tk >= 0 ? rowfac[tk + roff] : 0.f;
   }
   __syncthreads();
   switch ((ti.rows + 31) / 32) {  // uniform per block
@@ -420,14 +423,15 @@ bool fused_supported(int T, int H, int I) {
 
 hipError_t launch_prefill_fused(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
                                 const int32_t* sorted_slot, const _Float16* xh,
-                                const float* rowfac, uint16_t* hbuf, uint16_t* y, hipStream_t s) {
+                                const float* rowfac, int shared_rows, uint16_t* hbuf, uint16_t* y,
+                                hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const long S = (long)T * K + (hs ? T : 0);
   const long items = S / kPM + G;  // at most S/128 full row tiles plus one partial tile per group
   MOE_LAUNCH("grouped_ffn", s, k_prefill_ffn, dim3((unsigned)items), dim3(64 * kFNW), 0, s,
              W.gu_codes, W.gu_scales, W.dn_codes, W.dn_scales, W.scale2, xh, rowfac, offsets,
-             sorted_slot, T, K, H, I, G, hs, hbuf, y);
+             sorted_slot, T, K, H, I, G, hs, shared_rows, hbuf, y);
   return hipGetLastError();
 }
 

@@ -267,18 +267,20 @@ __global__ __launch_bounds__(64 * NW, 1) void k_prefill_gemm(
     const float* __restrict__ scale2, const uint16_t* __restrict__ asrc,
     const float* __restrict__ rowfac, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slot, int T, int K, int H, int I, int G, int has_shared,
-    uint16_t* __restrict__ out) {
+    int shared_rows, uint16_t* __restrict__ out) {
   constexpr int NTHR = 64 * NW;
   __shared__ __align__(16) PfSmem<NW> sm;
   const int NT = GU ? I / (32 * NW) : H / (64 * NW);  // N tiles per group
   PfTile ti;
   if (!pf_find_tile<NTHR>(offsets, G, 1, sm.base, sm.wsum, &ti)) return;  // item = row tile
   const int tid = threadIdx.x;
+  // gate_up: the shared group reads activation rows shared_rows + t (its own arm)
+  const int roff = (GU && has_shared && ti.g == G - 1) ? shared_rows : 0;
   for (int r = tid; r < kPM; r += NTHR) {
     int src = -1;
     if (r < ti.rows) {
       const int tk = slot_token(sorted_slot[ti.p0 + r], T, K, has_shared);
-      src = tk < 0 ? -1 : (GU ? tk : ti.p0 + r);
+      src = tk < 0 ? -1 : (GU ? tk + roff : ti.p0 + r);
     }
     sm.row_ok[r] = src >= 0;
     sm.row_src[r] = src >= 0 ? src : (GU ? 0 : ti.p0);  // a valid row to read for padding rows
@@ -302,7 +304,7 @@ void register_prefill_kernels(std::vector<const void*>& k) {
 
 hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
                               const int32_t* sorted_slot, const _Float16* xh, const float* rowfac,
-                              uint16_t* hbuf, uint16_t* y, hipStream_t s) {
+                              int shared_rows, uint16_t* hbuf, uint16_t* y, hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const long S = (long)T * K + (hs ? T : 0);
@@ -312,20 +314,20 @@ hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const in
   if (I % 256 == 0) {
     const dim3 g1((unsigned)mt_bound);
     MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<8, true>), g1, dim3(512), 0, s, W.gu_codes,
-               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
+               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, shared_rows, hbuf);
   } else {
     const dim3 g1((unsigned)mt_bound);
     MOE_LAUNCH("grouped_gate_up", s, (k_prefill_gemm<4, true>), g1, dim3(256), 0, s, W.gu_codes,
-               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, hbuf);
+               W.gu_scales, W.scale2, xa, rowfac, offsets, sorted_slot, T, K, H, I, G, hs, shared_rows, hbuf);
   }
   if (H % 512 == 0) {
     const dim3 g2((unsigned)mt_bound);
     MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<8, false>), g2, dim3(512), 0, s, W.dn_codes,
-               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
+               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, 0, y);
   } else {
     const dim3 g2((unsigned)mt_bound);
     MOE_LAUNCH("grouped_down", s, (k_prefill_gemm<4, false>), g2, dim3(256), 0, s, W.dn_codes,
-               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, y);
+               W.dn_scales, W.scale2, hbuf, nullptr, offsets, sorted_slot, T, K, H, I, G, hs, 0, y);
   }
   return hipGetLastError();
 }

@@ -84,19 +84,20 @@ hipError_t launch_xprep(const uint16_t* x, int T, int H, bool fp8, _Float16* xh,
                         uint8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_prefill_ffn(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
                               const int32_t* sorted_slot, const _Float16* xh, const float* rowfac,
-                              uint16_t* hbuf, uint16_t* y, hipStream_t s);
+                              int shared_rows, uint16_t* hbuf, uint16_t* y, hipStream_t s);
 // Fused gate_up -> SiLU -> down in one launch (moe_ffn_fused.hip) for the
 // shapes fused_supported() accepts; the two-launch grouped GEMM otherwise.
 void register_fused_kernels(std::vector<const void*>& k);
 bool fused_supported(int T, int H, int I);
 hipError_t launch_prefill_fused(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
                                 const int32_t* sorted_slot, const _Float16* xh,
-                                const float* rowfac, uint16_t* hbuf, uint16_t* y, hipStream_t s);
+                                const float* rowfac, int shared_rows, uint16_t* hbuf, uint16_t* y,
+                                hipStream_t s);
 bool decode_supported(int H, int I);
 size_t xprep_workspace_bytes(int T, int H);
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
-                             const int32_t* groups, bool fp8, uint16_t* hbuf, uint8_t* xq,
+                             const int32_t* groups, int act_mode, uint16_t* hbuf, uint8_t* xq,
                              float* xs, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

@@ -14,14 +14,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_ROW, MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_COMBINE,
-                   MOE_OP_PERMUTE, check)
+from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_ROUTED, MOE_ACT_FP8_ROW, MOE_ACT_FP8_SHARED,
+                   MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_COMBINE, MOE_OP_PERMUTE, check)
 
 __all__ = [
     "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
     "moe_combine", "moe_layer", "workspace_bytes", "moe_expert_ffn_noalloc", "MOE_ACT_BF16", "MOE_ACT_FP8_ROW",
     "NVFP4Router", "moe_router_topk", "moe_combine_gated", "moe_route_permute",
-    "moe_expert_ffn_combine",
+    "moe_expert_ffn_combine", "MOE_ACT_FP8_ROUTED", "MOE_ACT_FP8_SHARED",
 ]
 
 

@@ -62,6 +62,8 @@ extern "C" {
 /* Activation modes of moe_expert_ffn. */
 #define MOE_ACT_BF16 0        /* gate_up reads the bf16 activations as they are    */
 #define MOE_ACT_FP8_ROW 1     /* gate_up reads per-token-row e4m3 activations      */
+#define MOE_ACT_FP8_ROUTED 2  /* routed experts e4m3, the shared expert bf16       */
+#define MOE_ACT_FP8_SHARED 3  /* routed experts bf16, the shared expert e4m3       */
 
 /* Operation ids of moe_workspace_bytes. */
 #define MOE_OP_PERMUTE 1
@@ -236,6 +238,9 @@ int moe_route_permute(const float* logits, int T, int E, int K, int has_shared, 
  * quantisation of x: s_t = absmax(x[t]) / 448, q = e4m3_rne_sat(x[t] * (448 /
  * absmax)), and s_t multiplies the f32 sums of g and u (option (a) of the
  * issue above; weights stay exact, the e4m3 values enter the MFMA exactly).
+ * MOE_ACT_FP8_ROUTED applies it to the routed experts only, the shared expert
+ * reading the bf16 rows (arm S of the issue's shared-expert A/B table);
+ * MOE_ACT_FP8_SHARED is the mirror (routed bf16, shared e4m3).
  *
  *   W        host struct of device pointers, see moe_nvfp4_weights
  *   x        [T][H] bf16 bit patterns                (in)
@@ -252,9 +257,10 @@ int moe_route_permute(const float* logits, int T, int E, int K, int has_shared, 
  * Workspace contents after the call (S = T*K + T*has_shared, A(n) = n rounded
  * up to a multiple of 256): bytes [0, 2*S*I) hold h as bf16 [S][I] by sorted
  * position; with MOE_ACT_FP8_ROW the e4m3 codes [T][H] follow at byte
- * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H).  Scratch for
- * the grouped path's f16 activation rows [T][H] and their fp32 epilogue
- * factors [T] comes next (its contents are unspecified after a call).
+ * A(2*S*I) and the fp32 row scales [T] at A(2*S*I) + A(T*H) (with the
+ * per-class arms that region is scratch).  Scratch for the grouped path's
+ * f16 activation rows ([T][H], [2T][H] with a per-class arm) and their fp32
+ * epilogue factors comes next (its contents are unspecified after a call).
  */
 int moe_expert_ffn(const moe_nvfp4_weights* W, const uint16_t* x, int T, int K,
                    const int32_t* offsets, const int32_t* sorted_slot, const int32_t* groups,

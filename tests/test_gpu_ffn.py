@@ -25,6 +25,8 @@ from workloads import DECODE_TS, make_workload, workload_for
 pytestmark = pytest.mark.gpu
 
 GATE_BF16, GATE_FP8, GATE_TIGHT = 2e-2, 6e-2, 8e-3
+# act_mode of the C ABI -> the oracle's arm
+ARMS = {0: "bf16", 1: "fp8_row", 2: "fp8_routed", 3: "fp8_shared"}
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +43,7 @@ def _run(moe, wl, act_mode=0, W=None):
 
 def _full_check(moe, wl, act_mode=0, tag=""):
     r = _run(moe, wl, act_mode)
-    om = "fp8_row" if act_mode else "bf16"
+    om = ARMS[act_mode]
     exact = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
     emul = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K, act_mode=om,
                             h_round="bf16", y_round="bf16")
@@ -346,3 +348,20 @@ def test_long_prefill_full_size_sampled(moe):
 def test_fp8_arm_full_size_sampled(moe):
     _sampled_check(moe, "fp8_arm", act_mode=1)
     _sampled_check(moe, "fp8_arm", act_mode=0)
+
+
+@pytest.mark.parametrize("act_mode", [2, 3])
+@pytest.mark.parametrize("cfg", [
+    dict(name="decode", T=8, H=2048, E=512, K=10, I=512, has_shared=True),   # decode GEMV
+    dict(name="decode1", T=1, H=2048, E=512, K=10, I=512, has_shared=True),
+    dict(name="fused", T=300, H=2048, E=64, K=10, I=512, has_shared=True),   # fused prefill kernel
+    dict(name="twolaunch", T=700, H=256, E=4, K=2, I=128, has_shared=True),  # two-launch prefill
+    dict(name="noshared", T=40, H=512, E=16, K=4, I=256, has_shared=False),
+])
+def test_per_class_activation_arms(moe, cfg, act_mode):
+    """Routed e4m3 with the shared expert on bf16 (the A/B table's arm S), and
+    the mirror, against the oracle's arm, on every FFN path."""
+    cfg = dict(cfg)
+    name = cfg.pop("name")
+    wl = make_workload("arm", seed=21, x_kind="student_t", **cfg)
+    _full_check(moe, wl, act_mode=act_mode, tag=f"arm {act_mode} {name}")
