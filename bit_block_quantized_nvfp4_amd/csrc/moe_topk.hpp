@@ -45,74 +45,110 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(a, b);
 }
 
-// Route one token: `row` holds its E logits (global or LDS memory).  Lane k
-// < K writes slot k of ids_t / w_t (and of ids_copy when given, e.g. an LDS
-// copy for a consumer in the same block).  Every lane of the wave must call it.
-template <int MAXV>
-__device__ __forceinline__ void route_row_topk(const float* row, int E, int K, int32_t* ids_t,
-                                               float* w_t, int32_t* ids_copy = nullptr) {
+// Route R tokens with one wave: rows[r] holds token r's E logits (global or
+// LDS memory); tokens with live[r] false are skipped (uniform per wave).  Lane
+// k < K writes slot k of ids[r] / w[r] (and of ids_copy[r] when given, e.g. an
+// LDS copy for a consumer in the same block).  The R routes are independent
+// and their steps are interleaved (measured: two routes per wave cost about
+// two routes' time, so the kernels use R = 1).  Every lane of the wave must
+// call it.
+template <int MAXV, int R>
+__device__ __forceinline__ void route_rows_topk(const float* const (&rows)[R], const bool (&live)[R],
+                                                int E, int K, int32_t* const (&ids)[R],
+                                                float* const (&w)[R],
+                                                int32_t* const (&ids_copy)[R]) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[MAXV], jx[MAXV];  // key and slot j (expert lane + 64 j) of each entry
+  uint32_t key[R][MAXV], jx[R][MAXV];  // key and slot j (expert lane + 64 j) of each entry
 #pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int e = lane + 64 * j;
-    float z = -INFINITY;
-    if (e < E) z = row[e];
-    // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
-    key[j] = (e < E) ? logit_key((z != z) ? -INFINITY : z) : 0u;
-    jx[j] = (uint32_t)j;
-  }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int e = lane + 64 * j;
+      const bool in = live[r] && e < E;
+      float z = -INFINITY;
+      if (in) z = rows[r][e];
+      // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
+      key[r][j] = in ? logit_key((z != z) ? -INFINITY : z) : 0u;
+      jx[r][j] = (uint32_t)j;
+    }
   // largest key first; a swap only on a strictly larger key keeps equal keys
   // in ascending j, i.e. ascending expert index
 #pragma unroll
   for (int pass = 0; pass < MAXV; ++pass) {
 #pragma unroll
-    for (int i = pass & 1; i + 1 < MAXV; i += 2) {
-      const bool sw = key[i + 1] > key[i];
-      const uint32_t k0 = key[i], k1 = key[i + 1], j0 = jx[i], j1 = jx[i + 1];
-      key[i] = sw ? k1 : k0;
-      key[i + 1] = sw ? k0 : k1;
-      jx[i] = sw ? j1 : j0;
-      jx[i + 1] = sw ? j0 : j1;
-    }
-  }
-
-  float zsel = -INFINITY;
-  int isel = 0;
-  for (int k = 0; k < K; ++k) {
-    const uint32_t kmax = wave_max_u32(key[0]);
-    const bool has = key[0] == kmax;
-    const unsigned long long m = __ballot(has);
-    int win;  // expert index of the winner
-    if (__popcll(m) == 1) {
-      const int wl = __ffsll((long long)m) - 1;
-      win = wl + 64 * __builtin_amdgcn_readlane((int)jx[0], wl);
-    } else {
-      win = (int)wave_min_u32(has ? (uint32_t)lane + 64u * jx[0] : 0xFFFFFFFFu);
-    }
-    if (lane == k) {
-      zsel = key_logit(kmax);
-      isel = win;
-    }
-    if (lane == (win & 63)) {  // pop the head: the next largest becomes the head
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i + 1 < MAXV; ++i) {
-        key[i] = key[i + 1];
-        jx[i] = jx[i + 1];
+      for (int i = pass & 1; i + 1 < MAXV; i += 2) {
+        const bool sw = key[r][i + 1] > key[r][i];
+        const uint32_t k0 = key[r][i], k1 = key[r][i + 1], j0 = jx[r][i], j1 = jx[r][i + 1];
+        key[r][i] = sw ? k1 : k0;
+        key[r][i + 1] = sw ? k0 : k1;
+        jx[r][i] = sw ? j1 : j0;
+        jx[r][i + 1] = sw ? j0 : j1;
       }
-      key[MAXV - 1] = 0u;
+  }
+
+  float zsel[R];
+  int isel[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    zsel[r] = -INFINITY;
+    isel[r] = 0;
+  }
+  for (int k = 0; k < K; ++k) {
+    uint32_t kmax[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) kmax[r] = wave_max_u32(key[r][0]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool has = key[r][0] == kmax[r];
+      const unsigned long long m = __ballot(has);
+      int win;  // expert index of the winner
+      if (__popcll(m) == 1) {
+        const int wl = __ffsll((long long)m) - 1;
+        win = wl + 64 * __builtin_amdgcn_readlane((int)jx[r][0], wl);
+      } else {
+        win = (int)wave_min_u32(has ? (uint32_t)lane + 64u * jx[r][0] : 0xFFFFFFFFu);
+      }
+      if (lane == k) {
+        zsel[r] = key_logit(kmax[r]);
+        isel[r] = win;
+      }
+      if (lane == (win & 63)) {  // pop the head: the next largest becomes the head
+#pragma unroll
+        for (int i = 0; i + 1 < MAXV; ++i) {
+          key[r][i] = key[r][i + 1];
+          jx[r][i] = jx[r][i + 1];
+        }
+        key[r][MAXV - 1] = 0u;
+      }
     }
   }
 
-  const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zsel), 0));
-  float ex = 0.f;
-  if (lane < K) ex = expf(zsel == z0 ? 0.f : zsel - z0);
-  const float sum = wave_sum_dpp(ex);
-  if (lane < K) {
-    ids_t[lane] = isel;
-    w_t[lane] = ex / sum;
-    if (ids_copy) ids_copy[lane] = isel;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zsel[r]), 0));
+    float ex = 0.f;
+    if (lane < K) ex = expf(zsel[r] == z0 ? 0.f : zsel[r] - z0);
+    const float sum = wave_sum_dpp(ex);
+    if (live[r] && lane < K) {
+      ids[r][lane] = isel[r];
+      w[r][lane] = ex / sum;
+      if (ids_copy[r]) ids_copy[r][lane] = isel[r];
+    }
   }
+}
+
+// Route one token (route_rows_topk with R = 1).
+template <int MAXV>
+__device__ __forceinline__ void route_row_topk(const float* row, int E, int K, int32_t* ids_t,
+                                               float* w_t, int32_t* ids_copy = nullptr) {
+  const float* const rows[1] = {row};
+  const bool live[1] = {true};
+  int32_t* const ids[1] = {ids_t};
+  float* const ws[1] = {w_t};
+  int32_t* const cp[1] = {ids_copy};
+  route_rows_topk<MAXV, 1>(rows, live, E, K, ids, ws, cp);
 }
 
 }  // namespace moe
