@@ -214,11 +214,19 @@ constexpr int kDnPipe = 2;
 // conversion), 8 row factors, then per wave the gate and up scale runs
 // (2 x 16 x H/16 bytes).
 //
+// KS > 1 (split K, for launches whose units would not fill the chip): a block
+// is ONE unit and its KS = WPB waves take NCH / KS consecutive chunks each, so
+// every unit has KS waves' loads in flight instead of one.  The block's scale
+// runs are one LDS copy, each wave moving an equal piece of it; each wave's
+// partial sums go to LDS and wave 0 adds them in wave order (a fixed order:
+// the result does not depend on timing) before the epilogue.  LDS then holds
+// one pair of scale runs and (KS - 1) x 512 floats of partial sums.
+//
 // The activation rows are turned into the f16 MFMA operand in LDS, in place,
 // by the block itself (the rule of k_dec_xprep, bit for bit): wave wv converts
 // rows wv, wv + WPB, ...; the row's epilogue factor goes to LDS.  With FP8,
 // block 0 also writes the row codes and scales to xq / xs.
-template <int NCH, int WPB, int TR, bool FP8>
+template <int NCH, int WPB, int TR, bool FP8, int KS>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_gate_up(
     const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
     const float* __restrict__ scale2, const uint16_t* __restrict__ x,
@@ -229,9 +237,14 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
   constexpr int NDMA = (TR * CPR + 64 * WPB - 1) / (64 * WPB);
   constexpr int SRUN = 128 * NCH;                   // scale bytes of 16 rows
+  static_assert(KS == 1 || (KS == WPB && NCH % KS == 0 && KS % 2 == 0),
+                "split K: one unit per block, whole chunks per wave, whole scale runs per wave pair");
+  constexpr int NCK = NCH / KS;                     // chunks per wave
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
-  const int nbk = I / 16 / WPB;
-  const int a = blockIdx.x / nbk, pb = (blockIdx.x % nbk) * WPB + wv;
+  const int nbk = KS > 1 ? I / 16 : I / 16 / WPB;
+  const int a = blockIdx.x / nbk;
+  const int pb = KS > 1 ? blockIdx.x % nbk : (blockIdx.x % nbk) * WPB + wv;
+  const int c0 = KS > 1 ? wv * NCK : 0;             // this wave's first chunk
 
   // (1) activation rows (bf16) -> LDS, first of all: they do not depend on
   // the group, and issued ahead of every code load on the CU they land early,
@@ -338,14 +351,22 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     return;
   }
-  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
+  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (KS > 1 ? 0 : (size_t)wv * 2 * SRUN);
 
-  // the unit's scale runs -> LDS
+  // the unit's scale runs -> LDS (with split K, wave wv moves bytes
+  // [wv P, (wv + 1) P) of the gate run followed by the up run)
   const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
+  constexpr int SPIECE = KS > 1 ? 2 * SRUN / KS : SRUN;
   {
     const uint8_t* sg = gu_scales + grow * (H / 16);
-    dma_run<SRUN>(sg, sl, lane);
-    dma_run<SRUN>(sg + (size_t)I * (H / 16), sl + SRUN, lane);
+    if constexpr (KS == 1) {
+      dma_run<SRUN>(sg, sl, lane);
+      dma_run<SRUN>(sg + (size_t)I * (H / 16), sl + SRUN, lane);
+    } else {
+      const int off = wv * SPIECE;
+      dma_run<SPIECE>(off < SRUN ? sg + off : sg + (size_t)I * (H / 16) + (off - SRUN), sl + off,
+                      lane);
+    }
   }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the DMA
@@ -363,11 +384,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // while its later chunks stream in, instead of issuing all of them first
   // (the issue stalls once the memory pipeline is full, which delayed every
   // wave's first MFMA to late in the stream).
-  constexpr int D = NCH < kGuPipe ? NCH : kGuPipe;
+  constexpr int D = NCK < kGuPipe ? NCK : kGuPipe;
   const size_t rowb = (size_t)H / 2;
-  const uint8_t* cg = gu_codes + (grow + r16) * rowb + 16 * q;
+  const uint8_t* cg = gu_codes + (grow + r16) * rowb + 16 * q + 64 * c0;
   const uint8_t* cu = cg + (size_t)I * rowb;
-  u32x4 wg[NCH], wu[NCH];
+  u32x4 wg[NCK], wu[NCK];
   auto issue = [&](int c) {
     wg[c] = *(const u32x4*)(cg + 64 * c);
     wu[c] = *(const u32x4*)(cu + 64 * c);
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // (4) this wave's activation DMA is complete once at most the scale DMA,
   // the slot load and the first code loads are outstanding; the barrier
   // then covers the whole block.
-  constexpr int kScaleDma = 2 * (SRUN % 1024 == 0 ? SRUN / 1024 : SRUN / 256);
+  constexpr int kScaleDma = (KS > 1 ? 1 : 2) * (SPIECE % 1024 == 0 ? SPIECE / 1024 : SPIECE / 256);
   wait_vmcnt<kScaleDma + 1 + 2 * D>();
   __builtin_amdgcn_s_barrier();
 
@@ -402,18 +423,18 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // A row r16 of the MFMA = token r16; rows >= T read row T-1 (never stored)
   const int xr = r16 < T ? r16 : T - 1;
   const uint8_t* xrow = (const uint8_t*)xl;
-  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q + 8 * c0;
   // the swizzle touches only the low 4 bits of the chunk index, so the
   // operand of sub-MFMA (c, j) sits at aoff[j] + 256 c (an immediate offset)
   int aoff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) aoff[j] = swz_off(xr, 4 * q + j, CPR);
+  for (int j = 0; j < 4; ++j) aoff[j] = swz_off(xr, 4 * q + j, CPR) + 256 * c0;
   f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-  static_for<0, NCH>([&](auto ct) {
+  static_for<0, NCK>([&](auto ct) {
     constexpr int c = decltype(ct)::value;
-    // chunks issued so far: min(NCH, D + c); chunk c is complete once the
+    // chunks issued so far: min(NCK, D + c); chunk c is complete once the
     // ones after it are the only loads outstanding
-    constexpr int issued = D + c < NCH ? D + c : NCH;
+    constexpr int issued = D + c < NCK ? D + c : NCK;
     wait_vmcnt<2 * (issued - c - 1)>();
     const f16x2 sgv = e4m3x2_to_f16(*(const uint16_t*)(srow + 8 * c));
     const f16x2 suv = e4m3x2_to_f16(*(const uint16_t*)(srow + SRUN + 8 * c));
@@ -423,9 +444,31 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wg[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
       du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wu[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
     }
-    if constexpr (c + D < NCH) issue(c + D);
+    if constexpr (c + D < NCK) issue(c + D);
     __builtin_amdgcn_sched_barrier(0);
   });
+  if constexpr (KS > 1) {
+    // partial sums of waves 1 .. KS-1 -> LDS ([wave][8][64] floats, lane
+    // fastest); wave 0 adds them in wave order and runs the epilogue alone
+    float* red = (float*)(sl + 2 * SRUN);
+    if (wv > 0) {
+      float* dst = red + (size_t)(wv - 1) * 512 + lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[64 * i] = dg[i];
+        dst[64 * (4 + i)] = du[i];
+      }
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dg[i] += red[512 * w + 64 * i + lane];
+        du[i] += red[512 * w + 64 * (4 + i) + lane];
+      }
+  }
   uint16_t hv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -638,21 +681,24 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 void register_decode_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_dec_xprep<false>);
   k.push_back((const void*)&k_dec_xprep<true>);
-#define MOE_REG_GU3(NCH, WPB, TR)                                \
-  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, false>); \
-  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, true>);
-#define MOE_REG_GU2(NCH, WPB) \
-  MOE_REG_GU3(NCH, WPB, 1)    \
-  MOE_REG_GU3(NCH, WPB, 2)    \
-  MOE_REG_GU3(NCH, WPB, 4)    \
-  MOE_REG_GU3(NCH, WPB, 8)
-#define MOE_REG_GU(NCH) \
-  MOE_REG_GU2(NCH, 1)   \
-  MOE_REG_GU2(NCH, 4)
+#define MOE_REG_GU3(NCH, WPB, TR, KS)                                    \
+  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, false, KS>); \
+  k.push_back((const void*)&k_dec_gate_up<NCH, WPB, TR, true, KS>);
+#define MOE_REG_GU2(NCH, WPB, KS) \
+  MOE_REG_GU3(NCH, WPB, 1, KS)    \
+  MOE_REG_GU3(NCH, WPB, 2, KS)    \
+  MOE_REG_GU3(NCH, WPB, 4, KS)    \
+  MOE_REG_GU3(NCH, WPB, 8, KS)
+#define MOE_REG_GU(NCH)  \
+  MOE_REG_GU2(NCH, 1, 1) \
+  MOE_REG_GU2(NCH, 4, 1)
   MOE_REG_GU(2)
   MOE_REG_GU(4)
   MOE_REG_GU(8)
   MOE_REG_GU(16)
+  MOE_REG_GU2(4, 4, 4)
+  MOE_REG_GU2(8, 4, 4)
+  MOE_REG_GU2(16, 4, 4)
 #undef MOE_REG_GU
 #undef MOE_REG_GU2
 #undef MOE_REG_GU3
@@ -691,8 +737,8 @@ size_t xprep_workspace_bytes(int T, int H) {
   return align256((size_t)T * H * sizeof(_Float16)) + align256((size_t)T * sizeof(float));
 }
 
-// gate_up launch for one (NCH, WPB): picks the staged row count and the arm.
-template <int NCH, int WPB>
+// gate_up launch for one (NCH, WPB, KS): picks the staged row count and the arm.
+template <int NCH, int WPB, int KS>
 static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                                const int32_t* offsets, const int32_t* sorted_slot,
                                const int32_t* groups, int act_mode, uint8_t* xq, float* xs,
@@ -702,9 +748,11 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
   const int shared_g = W.has_shared ? W.E : -1;
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));  // activation rows staged
-  const size_t lds = (size_t)tr * H * 2 + 256 + (size_t)WPB * 2 * 16 * (H / 16);
-#define MOE_DEC_GU1(TR, F8)                                                                       \
-  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR, F8>), grid, dim3(64 * WPB), lds, s,  \
+  const size_t lds = (size_t)tr * H * 2 + 256 +
+                     (KS > 1 ? (size_t)2 * 16 * (H / 16) + (size_t)(KS - 1) * 512 * sizeof(float)
+                             : (size_t)WPB * 2 * 16 * (H / 16));
+#define MOE_DEC_GU1(TR, F8)                                                                           \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up<NCH, WPB, TR, F8, KS>), grid, dim3(64 * WPB), lds, s,  \
              W.gu_codes, W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, groups, T, K, H, \
              I, hs, fp8_sel, shared_g, hbuf)
 #define MOE_DEC_GU2(TR)                \
@@ -718,6 +766,29 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
   else MOE_DEC_GU2(8);
 #undef MOE_DEC_GU2
 #undef MOE_DEC_GU1
+}
+
+// Split K below this many gate_up units per CU (see k_dec_gate_up).
+constexpr long kGuSplitBelow = 2;
+
+template <int NCH>
+static void launch_gu_pick(bool split, int wpb, const moe_nvfp4_weights& W, const uint16_t* x,
+                           int T, int K, const int32_t* offsets, const int32_t* sorted_slot,
+                           const int32_t* groups, int act_mode, uint8_t* xq, float* xs,
+                           uint16_t* hbuf, long units, hipStream_t s) {
+  if constexpr (NCH % 4 == 0) {
+    if (split) {
+      launch_dec_gate_up<NCH, 4, 4>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs,
+                                    hbuf, dim3((unsigned)units), s);
+      return;
+    }
+  }
+  if (wpb == 4)
+    launch_dec_gate_up<NCH, 4, 1>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs,
+                                  hbuf, dim3((unsigned)(units / 4)), s);
+  else
+    launch_dec_gate_up<NCH, 1, 1>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs,
+                                  hbuf, dim3((unsigned)units), s);
 }
 
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
@@ -734,17 +805,15 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   // T=6: 22.3 vs 37 us), down from about 1.
   const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
   const long cus = num_cus();
+  // Fewer units than that: one unit per block with K split over 4 waves
+  // (H a multiple of 512).
   const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
   const int wpb_d = dn_units >= cus ? 4 : 1;
-  const dim3 g1((unsigned)(gu_units / wpb_g));
+  const bool split = gu_units < kGuSplitBelow * cus && (H / 128) % 4 == 0;
   const int nch = H / 128;
-#define MOE_DEC_GU(NCH)                                                                          \
-  do {                                                                                           \
-    if (wpb_g == 4)                                                                              \
-      launch_dec_gate_up<NCH, 4>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, hbuf, g1, s); \
-    else                                                                                         \
-      launch_dec_gate_up<NCH, 1>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, hbuf, g1, s); \
-  } while (0)
+#define MOE_DEC_GU(NCH)                                                                             \
+  launch_gu_pick<NCH>(split, wpb_g, W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, \
+                      hbuf, gu_units, s)
   if (nch == 2) MOE_DEC_GU(2);
   else if (nch == 4) MOE_DEC_GU(4);
   else if (nch == 8) MOE_DEC_GU(8);

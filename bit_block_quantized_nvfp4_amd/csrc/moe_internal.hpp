@@ -39,7 +39,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* 
 size_t permute_workspace_bytes(int T, int E, int K);
 // Batches up to this many tokens (one per wave) are routed and permuted by
 // one block.
-constexpr int kRouteFuseMaxT = 4;
+constexpr int kRouteFuseMaxT = 8;
 hipError_t launch_route_permute(const float* logits, int T, int E, int K, int has_shared,
                                 int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups, void* ws,

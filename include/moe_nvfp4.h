@@ -213,7 +213,7 @@ int moe_permute(const int32_t* ids, int T, int E, int K, int has_shared, int32_t
 
 /*
  * moe_route_topk followed by moe_permute, with the same outputs (ids, w and
- * the permutation arrays, bit for bit).  Batches of up to 4 tokens run as a
+ * the permutation arrays, bit for bit).  Batches of up to 8 tokens run as a
  * single kernel: one block routes them (a wave per token) and permutes the
  * ids from LDS, which takes a launch off the decode critical path; larger
  * batches run the two stages' own kernels.  ws: as moe_permute

@@ -1,5 +1,5 @@
 """GPU checks of the combined layer entry points: moe_route_permute (router
-top-K and permutation in one kernel for batches of up to 4 tokens, the two
+top-K and permutation in one kernel for batches of up to 8 tokens, the two
 kernels above) and moe_expert_ffn_combine (FFN then combine in one call).
 Both must reproduce the separate calls bit for bit -- they run the same
 arithmetic in the same order -- and the layer through them must pass the same
@@ -30,7 +30,7 @@ def _route_permute_both(moe, logits_np, K, E, has_shared):
 
 
 @pytest.mark.parametrize("E", [8, 100, 200, 512, 1000])
-@pytest.mark.parametrize("T", [1, 3, 4, 5, 16, 40])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 8, 9, 16, 40])
 def test_route_permute_matches_the_two_calls(moe, E, T):
     K = min(10, E)
     for hs in (False, True):
@@ -46,6 +46,23 @@ def test_route_permute_matches_the_two_calls(moe, E, T):
         want = oracle.permute(ids_o, E, hs)
         for g, w_, nm in zip(fused[2:6], want, names[2:6]):
             assert np.array_equal(g.cpu().numpy(), w_), nm
+
+
+@pytest.mark.parametrize("E,K", [(1024, 32), (32, 32), (40, 32), (1, 1), (2, 2)])
+def test_route_permute_largest_fused_batch(moe, E, K):
+    """8 tokens x K = 32 (256 slots, one per thread of the fused block), with
+    few experts (every group full) and the largest E."""
+    for T in (7, 8):
+        for hs in (False, True):
+            wl = make_workload("rpk", T=T, H=256, E=E, K=K, I=128, has_shared=hs, seed=E + K,
+                               with_weights=False)
+            fused, ref = _route_permute_both(moe, wl.logits, K, E, hs)
+            for a, b in zip(fused, ref):
+                assert torch.equal(a, b), f"E={E} K={K} T={T} shared={hs}"
+            ids_o, _ = oracle.route_topk(wl.logits, K)
+            want = oracle.permute(ids_o, E, hs)
+            for g, w_ in zip(fused[2:6], want):
+                assert np.array_equal(g.cpu().numpy(), w_)
 
 
 def test_route_permute_ties_and_nan(moe):
