@@ -27,7 +27,8 @@
 // group is even known.  f16 MFMA 16x16x32; weights are dequantised to f16
 // exactly with one instruction per element.
 //
-// k_dec_down: unit = (active group, 64 output rows as 4 MFMA blocks of 16);
+// k_dec_down: unit = (active group, 16 NB output rows as NB MFMA blocks of
+// 16; NB = 4, or fewer when the units would not fill the chip);
 // A = the group's h rows (bf16, by sorted position), up to 16 per pass, in
 // LDS, turned into f16 in place with a per-row power-of-two shift (undone in
 // the epilogue); f16 MFMA 16x16x32 against weights dequantised to f16 at one
@@ -489,55 +490,55 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 }
 
 // --------------------------------- down -----------------------------------
-// One wave = one unit (group, 64 output rows as 4 MFMA blocks of 16, all of
-// K = I); a block holds WPB consecutive units of one group and the group's h
-// rows (up to 16 per pass) in LDS, chunk-swizzled like the activations above.
-// Code loads are row-contiguous as in gate_up (lane (r16, q), chunk c: bytes
-// 64c + 16q of the row); the 64 rows' block scales are one contiguous run
-// that goes to LDS by DMA.  Every position of a group's range is a valid slot
-// (the permutation only places valid ones), so the rows are read without a
-// slot lookup; rows of a pass past the group's end repeat its last row and
-// are not stored.
+// One wave = one unit (group, 16 NB output rows as NB MFMA blocks of 16, all
+// of K = I); a block holds WPB consecutive units of one group and the group's
+// h rows (up to 16 per pass) in LDS, chunk-swizzled like the activations
+// above.  Code loads are row-contiguous as in gate_up (lane (r16, q), chunk
+// c: bytes 64c + 16q of the row); the unit's block scales are one contiguous
+// run that goes to LDS by DMA.  Every position of a group's range is a valid
+// slot (the permutation only places valid ones), so the rows are read without
+// a slot lookup.  Only the pass's valid rows are staged: the MFMA rows past
+// them read whatever the LDS holds, and their outputs (each output row
+// depends on its own A row only) are not stored.
 // Dynamic LDS: [16][I] h rows (bf16 as loaded, f16 after the conversion),
-// then per wave the scale run (64 x I/16 B), then the 16 rows' epilogue
+// then per wave the scale run (16 NB x I/16 B), then the 16 rows' epilogue
 // factors (f32).
-template <int NCH, int WPB>   // NCH = I / 128
+template <int NCH, int WPB, int NB>   // NCH = I / 128
 __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
     const float* __restrict__ scale2, const uint16_t* __restrict__ h,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ groups, int H, int I,
     uint16_t* __restrict__ y) {
   extern __shared__ __align__(16) uint16_t hl[];
-  constexpr int SRUN = 512 * NCH;  // scale bytes of 64 rows
+  constexpr int SRUN = 128 * NB * NCH;  // scale bytes of the unit's 16 NB rows
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r16 = lane & 15, q = lane >> 4;
   const int cpr = I / 8;
-  const int nbk = H / 64 / WPB;
+  const int nbk = H / (16 * NB) / WPB;
   const int a = blockIdx.x / nbk, rb = (blockIdx.x % nbk) * WPB + wv;
   const int nact = groups[0], e = groups[1 + a];
   asm volatile("" ::"s"(e));  // both lookups in one trip
   if (a >= nact) return;      // uniform per block
   const int p0 = offsets[e], n = offsets[e + 1] - p0;  // scalar loads, in flight meanwhile
   uint8_t* sl = (uint8_t*)hl + (size_t)16 * I * 2 + (size_t)wv * SRUN;
-  const size_t row0 = (size_t)e * H + (size_t)rb * 64;
+  const size_t row0 = (size_t)e * H + (size_t)rb * 16 * NB;
   const size_t rowb = (size_t)I / 2;
   const uint8_t* cr = dn_codes + (row0 + r16) * rowb + 16 * q;
-  u32x4 w[4][NCH];
+  u32x4 w[NB][NCH];
   // chunks [c0, c1) of every row block, issued in the order the MFMAs use them
   auto load_codes = [&](auto c0t, auto c1t) {
     constexpr int c0 = decltype(c0t)::value, c1 = decltype(c1t)::value;
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) w[nb][c] = *(const u32x4*)(cr + (size_t)nb * 16 * rowb + 64 * c);
+      for (int nb = 0; nb < NB; ++nb) w[nb][c] = *(const u32x4*)(cr + (size_t)nb * 16 * rowb + 64 * c);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // h rows [r0, r0 + 16) of the group -> LDS (rows past the end repeat the last)
+  // the group's valid h rows of [r0, r0 + 16) -> LDS
   auto stage = [&](int r0) {
-    const int last = (n - r0 < 16 ? n - r0 : 16) - 1;
-    dma_rows_swizzled(hl, 16, cpr, wv, WPB, lane, [&](int r) {
-      return (const uint8_t*)(h + (size_t)(p0 + r0 + (r < last ? r : last)) * I);
-    });
+    const int nv = n - r0 < 16 ? n - r0 : 16;
+    dma_rows_swizzled(hl, nv, cpr, wv, WPB, lane,
+                      [&](int r) { return (const uint8_t*)(h + (size_t)(p0 + r0 + r) * I); });
   };
   // Issue order: scale run, h rows of the first pass, the first DD code
   // chunks; the rest are issued one by one as the first pass consumes chunks
@@ -597,26 +598,26 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
       }
     }
   };
-  auto mfma_chunk = [&](f32x4 (&acc)[4], int c) {
-    f16x2 sc[4];
+  auto mfma_chunk = [&](f32x4 (&acc)[NB], int c) {
+    f16x2 sc[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
       sc[nb] = e4m3x2_to_f16(*(const uint16_t*)(srow + nb * 16 * (8 * NCH) + 8 * c));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f16x8 av = __builtin_bit_cast(f16x8, *(const u32x4*)(hrow + haoff[j] + 256 * c));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(w[nb][c][j], j < 2 ? sc[nb].x : sc[nb].y), acc[nb], 0, 0, 0);
     }
   };
-  auto epilogue = [&](const f32x4 (&acc)[4], int r0) {
+  auto epilogue = [&](const f32x4 (&acc)[NB], int r0) {
     float rf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) rf[i] = hfac[4 * q + i];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = rb * 64 + nb * 16 + r16;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = rb * 16 * NB + nb * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int mm = 4 * q + i;
@@ -626,9 +627,9 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   };
   // every code chunk loaded: one pass over all of them
   auto compute = [&](int r0) {
-    f32x4 acc[4];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       mfma_chunk(acc, c);
@@ -640,19 +641,19 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   };
   // this wave's DMAs are complete once only the first code chunks are
   // outstanding; the barrier covers the block
-  wait_vmcnt<4 * DD>();
+  wait_vmcnt<NB * DD>();
   __builtin_amdgcn_s_barrier();
   convert_h(0);
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   {  // first pass: chunk c once it has landed, then issue chunk c + DD
-    f32x4 acc[4];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     static_for<0, NCH>([&](auto ct) {
       constexpr int c = decltype(ct)::value;
       constexpr int issued = DD + c < NCH ? DD + c : NCH;
-      wait_vmcnt<4 * (issued - c - 1)>();
+      wait_vmcnt<NB * (issued - c - 1)>();
       mfma_chunk(acc, c);
       if constexpr (c + DD < NCH)
         load_codes(std::integral_constant<int, c + DD>(), std::integral_constant<int, c + DD + 1>());
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
     // the code words count as redefined on every pass, so the dequantised
     // operands (4x the registers of the codes) are not hoisted out of the loop
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) asm volatile("" : "+v"(w[nb][c]));
     compute(r0);
@@ -702,14 +703,16 @@ void register_decode_kernels(std::vector<const void*>& k) {
 #undef MOE_REG_GU
 #undef MOE_REG_GU2
 #undef MOE_REG_GU3
-  k.push_back((const void*)&k_dec_down<1, 1>);
-  k.push_back((const void*)&k_dec_down<1, 4>);
-  k.push_back((const void*)&k_dec_down<2, 1>);
-  k.push_back((const void*)&k_dec_down<2, 4>);
-  k.push_back((const void*)&k_dec_down<4, 1>);
-  k.push_back((const void*)&k_dec_down<4, 4>);
-  k.push_back((const void*)&k_dec_down<8, 1>);
-  k.push_back((const void*)&k_dec_down<8, 4>);
+#define MOE_REG_DN(NCH)                              \
+  k.push_back((const void*)&k_dec_down<NCH, 4, 4>); \
+  k.push_back((const void*)&k_dec_down<NCH, 4, 2>); \
+  k.push_back((const void*)&k_dec_down<NCH, 4, 1>);
+  k.push_back((const void*)&k_dec_down<1, 4, 4>);
+  k.push_back((const void*)&k_dec_down<1, 4, 2>);
+  MOE_REG_DN(2)
+  MOE_REG_DN(4)
+  MOE_REG_DN(8)
+#undef MOE_REG_DN
 }
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -770,6 +773,11 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
 
 // Split K below this many gate_up units per CU (see k_dec_gate_up).
 constexpr long kGuSplitBelow = 2;
+// Down units of 64 rows from this many per CU on, else of 32 or 16 rows
+// (measured at H=2048, I=512, down us with the threshold at 0 / 4 / 8 / 16:
+// T=1 7.1 / 6.9 / 6.5 / 6.3, T=4 10.4 / 10.1 / 9.6 / 9.2, T=8 13.7 / 13.4 /
+// 13.5 / 12.3).
+constexpr long kDnWavesPerCu = 16;
 
 template <int NCH>
 static void launch_gu_pick(bool split, int wpb, const moe_nvfp4_weights& W, const uint16_t* x,
@@ -798,17 +806,15 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
   const int G = W.E + hs;
   const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
-  // Waves (units) per block: 4 (one staged copy of the activation or h rows
-  // per 4 units) once the units are plentiful, else 1 so that small T still
-  // spreads over many CUs.  Measured crossovers (H=2048, I=512, 256 CUs):
-  // gate_up gains from 4 from about 2 units per CU on (T=3: 15.8 vs 17.8 us,
-  // T=6: 22.3 vs 37 us), down from about 1.
+  // gate_up waves (units) per block: 4 (one staged copy of the activation
+  // rows per 4 units) once the units are plentiful, else 1 so that small T
+  // still spreads over many CUs (measured at H=2048, I=512, 256 CUs: 4 gains
+  // from about 2 units per CU on, T=3: 15.8 vs 17.8 us, T=6: 22.3 vs 37 us);
+  // fewer than kGuSplitBelow units per CU: one unit per block with K split
+  // over 4 waves (H a multiple of 512).
   const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
   const long cus = num_cus();
-  // Fewer units than that: one unit per block with K split over 4 waves
-  // (H a multiple of 512).
   const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
-  const int wpb_d = dn_units >= cus ? 4 : 1;
   const bool split = gu_units < kGuSplitBelow * cus && (H / 128) % 4 == 0;
   const int nch = H / 128;
 #define MOE_DEC_GU(NCH)                                                                             \
@@ -820,23 +826,31 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   else if (nch == 16) MOE_DEC_GU(16);
   else return hipErrorInvalidValue;
 #undef MOE_DEC_GU
-  const dim3 g2((unsigned)(dn_units / wpb_d)), b2(64 * wpb_d);
-  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)wpb_d * 64 * (I / 16) + 16 * sizeof(float);
+  // Down rows per wave: 64 (4 MFMA blocks) once that gives kDnWavesPerCu
+  // waves per CU, else 32 or 16 (more, shorter units at small T).
+  // (A block is 4 waves = 64 NB rows of one group either way.)
+  int nb_d = dn_units >= kDnWavesPerCu * cus ? 4 : (2 * dn_units >= kDnWavesPerCu * cus ? 2 : 1);
+  if (nb_d * I < 256) nb_d = 2;  // the unit's scale run is whole DMA instructions (I = 128)
+  const dim3 g2((unsigned)(dn_units * 4 / nb_d / 4)), b2(256);
+  const size_t lds_dn = (size_t)16 * I * sizeof(uint16_t) + (size_t)4 * nb_d * I + 16 * sizeof(float);
   const int ncd = I / 128;
-#define MOE_DEC_DN(NCH)                                                                            \
-  do {                                                                                             \
-    if (wpb_d == 4)                                                                                \
-      MOE_LAUNCH("dec_down", s, (k_dec_down<NCH, 4>), g2, b2, lds_dn, s, W.dn_codes, W.dn_scales,       \
-                 W.scale2, hbuf, offsets, groups, H, I, y);                 \
-    else                                                                                           \
-      MOE_LAUNCH("dec_down", s, (k_dec_down<NCH, 1>), g2, b2, lds_dn, s, W.dn_codes, W.dn_scales,       \
-                 W.scale2, hbuf, offsets, groups, H, I, y);                 \
+#define MOE_DEC_DN2(NCH, WPB, NB)                                                                 \
+  MOE_LAUNCH("dec_down", s, (k_dec_down<NCH, WPB, NB>), g2, b2, lds_dn, s, W.dn_codes, W.dn_scales, \
+             W.scale2, hbuf, offsets, groups, H, I, y)
+#define MOE_DEC_DN(NCH)                          \
+  do {                                           \
+    if (nb_d == 4) MOE_DEC_DN2(NCH, 4, 4);       \
+    else if (nb_d == 2) MOE_DEC_DN2(NCH, 4, 2);  \
+    else MOE_DEC_DN2(NCH, 4, 1);                 \
   } while (0)
-  if (ncd == 1) MOE_DEC_DN(1);
-  else if (ncd == 2) MOE_DEC_DN(2);
+  if (ncd == 1) {
+    if (nb_d == 4) MOE_DEC_DN2(1, 4, 4);
+    else MOE_DEC_DN2(1, 4, 2);
+  } else if (ncd == 2) MOE_DEC_DN(2);
   else if (ncd == 4) MOE_DEC_DN(4);
   else if (ncd == 8) MOE_DEC_DN(8);
   else return hipErrorInvalidValue;
+#undef MOE_DEC_DN2
 #undef MOE_DEC_DN
   return hipGetLastError();
 }
