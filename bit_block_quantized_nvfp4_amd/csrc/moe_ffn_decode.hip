@@ -209,6 +209,93 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kGuPipe = 2;
 constexpr int kDnPipe = 2;
 
+// Activation rows -> f16 MFMA operand in LDS, in place (the rule of
+// k_dec_xprep, bit for bit): wave wv of WPB converts rows wv, wv + WPB, ...
+// of the TR staged rows (chunk-swizzled, CPR 16-byte chunks per row); the
+// row's epilogue factor goes to fac[]; with fp8_row, the row is quantised to
+// e4m3 (and with write_q its codes and scale go to xq / xs).
+template <int CPR, int TR, int WPB>
+__device__ __forceinline__ void dec_convert_rows(_Float16* xl, float* fac, float* __restrict__ xs,
+                                                 uint8_t* __restrict__ xq, int H, int T,
+                                                 bool fp8_row, bool write_q, int wv, int lane) {
+  constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
+  for (int r = wv; r < TR; r += WPB) {
+    float amax = 0.f;
+    {
+      u32x4 v[NCL];
+#pragma unroll
+      for (int k = 0; k < NCL; ++k) {
+        const int ch = lane + 64 * k;
+        v[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                        : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < NCL; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
+        }
+    }
+    amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
+    float mul, rf;
+    if (fp8_row) {
+      rf = amax > 0.f ? amax / 448.0f : 1.0f;
+      mul = amax > 0.f ? 448.0f / amax : 1.0f;
+    } else {
+      const int sh = f16_row_shift(amax);
+      mul = ldexpf(1.0f, sh);
+      rf = ldexpf(1.0f, -sh);
+    }
+    const bool wr = write_q && fp8_row && r < T;
+    if (lane == 0) {
+      fac[r] = rf;
+      if (wr) xs[r] = rf;
+    }
+    u32x4 vr[NCL];
+#pragma unroll
+    for (int k = 0; k < NCL; ++k) {
+      const int ch = lane + 64 * k;
+      vr[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < NCL; ++k) {
+      const int ch = lane + 64 * k;
+      if (ch >= CPR) break;
+      uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
+      const u32x4 v = vr[k];
+      u32x4 o;
+      if (fp8_row) {
+        u32x2 code;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float f0 = bf16_bits_to_f32(v[2 * j] & 0xFFFFu) * mul;
+          float f1 = bf16_bits_to_f32(v[2 * j] >> 16) * mul;
+          float f2 = bf16_bits_to_f32(v[2 * j + 1] & 0xFFFFu) * mul;
+          float f3 = bf16_bits_to_f32(v[2 * j + 1] >> 16) * mul;
+          f0 = fminf(fmaxf(f0, -448.f), 448.f);
+          f1 = fminf(fmaxf(f1, -448.f), 448.f);
+          f2 = fminf(fmaxf(f2, -448.f), 448.f);
+          f3 = fminf(fmaxf(f3, -448.f), 448.f);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
+          code[j] = (uint32_t)w;
+        }
+        if (wr) *(u32x2*)(xq + (size_t)r * H + 8 * ch) = code;
+        const u32x2 lo = fp8x4_to_f16(code.x), hi = fp8x4_to_f16(code.y);
+        o = u32x4{lo.x, lo.y, hi.x, hi.y};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xFFFFu) * mul,
+                            bf16_bits_to_f32(v[j] >> 16) * mul);
+      }
+      *(u32x4*)pch = o;
+    }
+  }
+}
+
 // TR = activation rows staged (T rounded up to 1, 2, 4 or 8; rows >= T repeat
 // row T-1), which makes the number of DMA instructions per wave a constant.
 // Dynamic LDS: [TR][H] activation rows (bf16 as loaded, f16 after the in-place
@@ -264,82 +351,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
   // row's epilogue factor goes to fac[]; with FP8, block 0 also writes the
   // row codes and scales to xq / xs.
   auto convert_rows = [&](bool fp8_row) {
-    constexpr int NCL = (CPR + 63) / 64;  // chunks of a row per lane
-    for (int r = wv; r < TR; r += WPB) {
-      float amax = 0.f;
-      {
-        u32x4 v[NCL];
-#pragma unroll
-        for (int k = 0; k < NCL; ++k) {
-          const int ch = lane + 64 * k;
-          v[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
-                          : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int k = 0; k < NCL; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] & 0xFFFFu)));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][j] >> 16)));
-          }
-      }
-      amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
-      float mul, rf;
-      if (fp8_row) {
-        rf = amax > 0.f ? amax / 448.0f : 1.0f;
-        mul = amax > 0.f ? 448.0f / amax : 1.0f;
-      } else {
-        const int sh = f16_row_shift(amax);
-        mul = ldexpf(1.0f, sh);
-        rf = ldexpf(1.0f, -sh);
-      }
-      const bool wr = fp8_row && fp8_sel == 0 && blockIdx.x == 0 && r < T;
-      if (lane == 0) {
-        fac[r] = rf;
-        if (wr) xs[r] = rf;
-      }
-      u32x4 vr[NCL];
-#pragma unroll
-      for (int k = 0; k < NCL; ++k) {
-        const int ch = lane + 64 * k;
-        vr[k] = ch < CPR ? *(const u32x4*)((const uint8_t*)xl + swz_off(r, ch, CPR))
-                         : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int k = 0; k < NCL; ++k) {
-        const int ch = lane + 64 * k;
-        if (ch >= CPR) break;
-        uint8_t* pch = (uint8_t*)xl + swz_off(r, ch, CPR);
-        const u32x4 v = vr[k];
-        u32x4 o;
-        if (fp8_row) {
-          u32x2 code;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float f0 = bf16_bits_to_f32(v[2 * j] & 0xFFFFu) * mul;
-            float f1 = bf16_bits_to_f32(v[2 * j] >> 16) * mul;
-            float f2 = bf16_bits_to_f32(v[2 * j + 1] & 0xFFFFu) * mul;
-            float f3 = bf16_bits_to_f32(v[2 * j + 1] >> 16) * mul;
-            f0 = fminf(fmaxf(f0, -448.f), 448.f);
-            f1 = fminf(fmaxf(f1, -448.f), 448.f);
-            f2 = fminf(fmaxf(f2, -448.f), 448.f);
-            f3 = fminf(fmaxf(f3, -448.f), 448.f);
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, w, true);
-            code[j] = (uint32_t)w;
-          }
-          if (wr) *(u32x2*)(xq + (size_t)r * H + 8 * ch) = code;
-          const u32x2 lo = fp8x4_to_f16(code.x), hi = fp8x4_to_f16(code.y);
-          o = u32x4{lo.x, lo.y, hi.x, hi.y};
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            o[j] = pack_f16x2(bf16_bits_to_f32(v[j] & 0xFFFFu) * mul,
-                              bf16_bits_to_f32(v[j] >> 16) * mul);
-        }
-        *(u32x4*)pch = o;
-      }
-    }
+    dec_convert_rows<CPR, TR, WPB>(xl, fac, xs, xq, H, T, fp8_row, fp8_sel == 0 && blockIdx.x == 0,
+                                   wv, lane);
   };
   // a < min(T*K + S, E') <= E', so groups[1 + a] is in bounds; both words in one trip
   const int nact = groups[0], e = groups[1 + a];
@@ -486,6 +499,157 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
       const int i = tok & 3;
       h[(size_t)(p0 + p) * I + j] = i == 0 ? hv[0] : (i == 1 ? hv[1] : (i == 2 ? hv[2] : hv[3]));
     }
+  }
+}
+
+// Whole-CU gate_up: one block of kGuCuWaves waves per CU stages and converts
+// the activation rows once and takes an equal share (within one unit) of the
+// launch's active units, split at run time from the active group count; wave
+// w takes units u0 + w, u0 + w + kGuCuWaves, ... of its block's share.  Each
+// CU then streams the same amount of weights: with blocks of 4 units, 2.5
+// blocks per CU on average leave some CUs with 3 blocks and others with 2,
+// and the kernel waits for the CUs with 3 (measured at T=8: 18.0 us against
+// 13.4 us).  The unit itself is k_dec_gate_up's (same loads, pipeline, MFMAs
+// and epilogue, so the same bits).  All units of a block read one activation
+// form, so the per-class FP8 arms keep k_dec_gate_up.
+constexpr int kGuCuWaves = 16;
+
+template <int NCH, int TR, bool FP8>
+__global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_gate_up_cu(
+    const uint8_t* __restrict__ gu_codes, const uint8_t* __restrict__ gu_scales,
+    const float* __restrict__ scale2, const uint16_t* __restrict__ x,
+    uint8_t* __restrict__ xq, float* __restrict__ xs, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_slot, const int32_t* __restrict__ groups, int T, int K,
+    int H, int I, int has_shared, uint16_t* __restrict__ h) {
+  constexpr int WPB = kGuCuWaves;
+  extern __shared__ __align__(16) _Float16 xl[];
+  constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
+  constexpr int NDMA = (TR * CPR + 64 * WPB - 1) / (64 * WPB);
+  constexpr int SRUN = 128 * NCH;                   // scale bytes of 16 rows
+  constexpr int D = NCH < kGuPipe ? NCH : kGuPipe;
+  constexpr int kScaleDma = 2 * (SRUN % 1024 == 0 ? SRUN / 1024 : SRUN / 256);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // (1) activation rows (bf16) -> LDS, first of all (every wave)
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int base = 64 * (wv + WPB * i), L = base + lane;
+    if (L < TR * CPR) {
+      const int r = L / CPR, ch = (L % CPR) ^ (r & 15);
+      dma16(x + (size_t)(r < T ? r : T - 1) * H + 8 * ch, (uint8_t*)xl + 16 * base);
+    }
+  }
+  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
+  uint8_t* sl = (uint8_t*)xl + (size_t)TR * H * 2 + 256 + (size_t)wv * 2 * SRUN;
+
+  // (2) this block's share of the active units
+  const int nbk = I / 16;
+  const int units = groups[0] * nbk;
+  const int u0 = (int)((long long)blockIdx.x * units / gridDim.x);
+  const int u1 = (int)((long long)(blockIdx.x + 1) * units / gridDim.x);
+
+  // per-unit state: the unit's group, metadata, code pointers and words
+  const size_t rowb = (size_t)H / 2;
+  int e = 0, pb = 0, p0 = 0, n = 1, slot_l = 0;
+  float s2g = 0.f, s2u = 0.f;
+  const uint8_t* cg = gu_codes;
+  const uint8_t* cu = gu_codes;
+  u32x4 wg[NCH], wu[NCH];
+  auto issue = [&](int c) {
+    wg[c] = *(const u32x4*)(cg + 64 * c);
+    wu[c] = *(const u32x4*)(cu + 64 * c);
+  };
+  // the unit's scale runs (DMA), its metadata and slot, and its first D code
+  // chunks, in that order
+  auto begin_unit = [&](int uu) {
+    const int a = uu / nbk;
+    pb = uu % nbk;
+    e = groups[1 + a];
+    const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
+    const uint8_t* sg = gu_scales + grow * (H / 16);
+    dma_run<SRUN>(sg, sl, lane);
+    dma_run<SRUN>(sg + (size_t)I * (H / 16), sl + SRUN, lane);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    p0 = offsets[e];
+    n = offsets[e + 1] - p0;
+    s2g = scale2[3 * e + 0];
+    s2u = scale2[3 * e + 1];
+    slot_l = sorted_slot[p0 + (lane < n ? lane : n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    cg = gu_codes + (grow + r16) * rowb + 16 * q;
+    cu = cg + (size_t)I * rowb;
+#pragma unroll
+    for (int c = 0; c < D; ++c) issue(c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const bool has = u0 + wv < u1;  // uniform per wave
+  if (has) begin_unit(u0 + wv);
+  // this wave's activation DMA is complete once at most its scale DMA, slot
+  // load and first code loads are outstanding; the barrier covers the block
+  if (has) wait_vmcnt<kScaleDma + 1 + 2 * D>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  dec_convert_rows<CPR, TR, WPB>(xl, fac, xs, xq, H, T, FP8, FP8 && blockIdx.x == 0, wv, lane);
+  if (has) wait_vmcnt<2 * D>();  // the scale runs and the slot have landed
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  if (!has) return;
+
+  float ums[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ums[t] = fac[t < TR ? t : TR - 1];
+  const int xr = r16 < T ? r16 : T - 1;
+  const uint8_t* xrow = (const uint8_t*)xl;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = swz_off(xr, 4 * q + j, CPR);
+  // the MFMAs of the unit (chunk c once it has landed, then chunk c + D is
+  // issued) and its epilogue
+  auto compute_unit = [&]() {
+    f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+    static_for<0, NCH>([&](auto ct) {
+      constexpr int c = decltype(ct)::value;
+      constexpr int issued = D + c < NCH ? D + c : NCH;
+      wait_vmcnt<2 * (issued - c - 1)>();
+      const f16x2 sgv = e4m3x2_to_f16(*(const uint16_t*)(srow + 8 * c));
+      const f16x2 suv = e4m3x2_to_f16(*(const uint16_t*)(srow + SRUN + 8 * c));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 av = *(const f16x8*)(xrow + aoff[j] + 256 * c);
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wg[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
+        du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wu[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
+      }
+      if constexpr (c + D < NCH) issue(c + D);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    uint16_t hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float um = q == 0 ? ums[i] : (q == 1 ? ums[4 + i] : 0.f);  // tokens >= 8 are never stored
+      const float g = dg[i] * um * s2g, u = du[i] * um * s2u;
+      hv[i] = f32_to_bf16_bits(silu_f32(g) * u);
+    }
+    const int tokl = slot_token(slot_l, T, K, has_shared);
+    const int j = pb * 16 + r16;
+    for (int p = 0; p < n; ++p) {
+      const int tok = p < 64 ? __shfl(tokl, p, 64) : slot_token(sorted_slot[p0 + p], T, K, has_shared);
+      if (tok >= 0 && (tok >> 2) == q) {
+        const int i = tok & 3;
+        h[(size_t)(p0 + p) * I + j] = i == 0 ? hv[0] : (i == 1 ? hv[1] : (i == 2 ? hv[2] : hv[3]));
+      }
+    }
+  };
+  compute_unit();
+  // further units of the share (when it exceeds one per wave): the wave's
+  // own scale slot is reused once its reads are done
+  for (int uu = u0 + wv + WPB; uu < u1; uu += WPB) {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+    begin_unit(uu);
+    wait_vmcnt<2 * D>();
+    compute_unit();
   }
 }
 
@@ -700,6 +864,20 @@ void register_decode_kernels(std::vector<const void*>& k) {
   MOE_REG_GU2(4, 4, 4)
   MOE_REG_GU2(8, 4, 4)
   MOE_REG_GU2(16, 4, 4)
+#define MOE_REG_GUC2(NCH, TR)                                    \
+  k.push_back((const void*)&k_dec_gate_up_cu<NCH, TR, false>); \
+  k.push_back((const void*)&k_dec_gate_up_cu<NCH, TR, true>);
+#define MOE_REG_GUC(NCH) \
+  MOE_REG_GUC2(NCH, 1)   \
+  MOE_REG_GUC2(NCH, 2)   \
+  MOE_REG_GUC2(NCH, 4)   \
+  MOE_REG_GUC2(NCH, 8)
+  MOE_REG_GUC(2)
+  MOE_REG_GUC(4)
+  MOE_REG_GUC(8)
+  MOE_REG_GUC(16)
+#undef MOE_REG_GUC
+#undef MOE_REG_GUC2
 #undef MOE_REG_GU
 #undef MOE_REG_GU2
 #undef MOE_REG_GU3
@@ -773,6 +951,35 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
 
 // Split K below this many gate_up units per CU (see k_dec_gate_up).
 constexpr long kGuSplitBelow = 2;
+// Whole-CU gate_up blocks (k_dec_gate_up_cu) from this many units per CU on.
+constexpr long kGuCuFrom = 4;
+
+// The whole-CU gate_up launch: one block per CU.
+template <int NCH>
+static void launch_gu_cu(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                         const int32_t* offsets, const int32_t* sorted_slot,
+                         const int32_t* groups, int act_mode, uint8_t* xq, float* xs,
+                         uint16_t* hbuf, hipStream_t s) {
+  const bool fp8 = act_mode != MOE_ACT_BF16;
+  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
+  const size_t lds = (size_t)tr * H * 2 + 256 + (size_t)kGuCuWaves * 2 * 16 * (H / 16);
+  const dim3 grid((unsigned)num_cus()), block(64 * kGuCuWaves);
+#define MOE_DEC_GUC1(TR, F8)                                                                     \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_gate_up_cu<NCH, TR, F8>), grid, block, lds, s, W.gu_codes, \
+             W.gu_scales, W.scale2, x, xq, xs, offsets, sorted_slot, groups, T, K, H, I, hs, hbuf)
+#define MOE_DEC_GUC2(TR)              \
+  do {                                \
+    if (fp8) MOE_DEC_GUC1(TR, true);  \
+    else MOE_DEC_GUC1(TR, false);     \
+  } while (0)
+  if (tr == 1) MOE_DEC_GUC2(1);
+  else if (tr == 2) MOE_DEC_GUC2(2);
+  else if (tr == 4) MOE_DEC_GUC2(4);
+  else MOE_DEC_GUC2(8);
+#undef MOE_DEC_GUC2
+#undef MOE_DEC_GUC1
+}
 // Down units of 64 rows from this many per CU on, else of 32 or 16 rows
 // (measured at H=2048, I=512, down us with the threshold at 0 / 4 / 8 / 16:
 // T=1 7.1 / 6.9 / 6.5 / 6.3, T=4 10.4 / 10.1 / 9.6 / 9.2, T=8 13.7 / 13.4 /
@@ -780,10 +987,14 @@ constexpr long kGuSplitBelow = 2;
 constexpr long kDnWavesPerCu = 16;
 
 template <int NCH>
-static void launch_gu_pick(bool split, int wpb, const moe_nvfp4_weights& W, const uint16_t* x,
-                           int T, int K, const int32_t* offsets, const int32_t* sorted_slot,
-                           const int32_t* groups, int act_mode, uint8_t* xq, float* xs,
-                           uint16_t* hbuf, long units, hipStream_t s) {
+static void launch_gu_pick(bool split, int wpb, bool cu_mode, const moe_nvfp4_weights& W,
+                           const uint16_t* x, int T, int K, const int32_t* offsets,
+                           const int32_t* sorted_slot, const int32_t* groups, int act_mode,
+                           uint8_t* xq, float* xs, uint16_t* hbuf, long units, hipStream_t s) {
+  if (cu_mode) {
+    launch_gu_cu<NCH>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, hbuf, s);
+    return;
+  }
   if constexpr (NCH % 4 == 0) {
     if (split) {
       launch_dec_gate_up<NCH, 4, 4>(W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs,
@@ -816,10 +1027,14 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
   const long cus = num_cus();
   const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
   const bool split = gu_units < kGuSplitBelow * cus && (H / 128) % 4 == 0;
+  // whole-CU blocks once every CU gets several units (one activation form
+  // per block: the bf16 arm or the FP8 row arm)
+  const bool cu_mode = !split && gu_units >= kGuCuFrom * cus &&
+                       (act_mode == MOE_ACT_BF16 || act_mode == MOE_ACT_FP8_ROW);
   const int nch = H / 128;
 #define MOE_DEC_GU(NCH)                                                                             \
-  launch_gu_pick<NCH>(split, wpb_g, W, x, T, K, offsets, sorted_slot, groups, act_mode, xq, xs, \
-                      hbuf, gu_units, s)
+  launch_gu_pick<NCH>(split, wpb_g, cu_mode, W, x, T, K, offsets, sorted_slot, groups, act_mode, \
+                      xq, xs, hbuf, gu_units, s)
   if (nch == 2) MOE_DEC_GU(2);
   else if (nch == 4) MOE_DEC_GU(4);
   else if (nch == 8) MOE_DEC_GU(8);
