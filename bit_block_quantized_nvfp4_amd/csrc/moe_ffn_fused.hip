@@ -53,6 +53,10 @@ constexpr int kFNH = kFNB / 2;     // gate (or up) n-blocks of a gate_up wave
 constexpr int kFWR = 16 * kFNB * kFNW;  // weight rows per N tile (512)
 constexpr int kFARow = 2 * kFK;    // bytes of one A row per step
 constexpr int kFSRow = kFK / 16;   // scale bytes of one weight row per step
+// Consecutive items per XCD (pf_item_of_block).  Measured, fused FFN at
+// T=4096 / T=8192 (FP8 arm): 524 / 881 us with 1, 520 / 880 with 2, 515 /
+// 846 with 4, 514 / 869 with 8.
+constexpr int kFusedXcdRun = 4;
 
 struct FfnSmem {
   uint8_t A[2][kPM * kFARow];        // A tile of a step (rows x 512 B), chunks swizzled by (row & 15)
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(64 * kFNW, 1) void k_prefill_ffn(
   // shared_rows + t (its own activation arm) when shared_rows > 0
   const uint32_t xbytes = (uint32_t)(T + shared_rows) * (uint32_t)H * 2u;  // < 2^31 (fused_supported)
   PfTile ti;
-  if (!pf_find_tile<NTHR>(offsets, G, 1, sm.base, sm.wsum, &ti)) return;
+  if (!pf_find_tile<NTHR>(offsets, G, 1, sm.base, sm.wsum, &ti, kFusedXcdRun)) return;
   const int roff = (has_shared && ti.g == G - 1) ? shared_rows : 0;
   for (int r = threadIdx.x; r < kPM; r += NTHR) {
     int tk = -1;

@@ -53,9 +53,24 @@ __device__ __forceinline__ int pf_field(unsigned long long v, int k) {
   return k == 0 ? (int)(v & 0x7FFFFFFFull) : (int)((v >> (31 + 11 * (k - 1))) & 0x7FFull);
 }
 
+// Item of block b of nb when runs of R consecutive items go to one XCD:
+// blocks are dealt to the 8 XCDs in turn (block b to XCD b % 8), so block
+// (q R + r) 8 + x takes item (q 8 + x) R + r, i.e. XCD x runs items
+// (q 8 + x) R .. + R - 1 back to back; the tail past the last whole run of
+// 8 R blocks keeps item = block.  A bijection on [0, nb), and the items
+// still start in about their list order.  Adjacent items of one group then
+// share the XCD's L2 for their weight stream.
+__device__ __forceinline__ int pf_item_of_block(int b, int nb, int R) {
+  const int M = nb / (8 * R) * (8 * R);
+  if (R <= 1 || b >= M) return b;
+  const int x = b % 8, s = b / 8;
+  return ((s / R) * 8 + x) * R + s % R;
+}
+
 template <int NTHR>
 __device__ __forceinline__ bool pf_find_tile(const int32_t* __restrict__ offsets, int G, int NT,
-                             unsigned long long* base, unsigned long long* wsum, PfTile* ti) {
+                             unsigned long long* base, unsigned long long* wsum, PfTile* ti,
+                             int xcd_run = 1) {
   constexpr int NWV = NTHR / 64;
   const int tid = threadIdx.x;
   for (int g = tid; g < G; g += NTHR) {
@@ -87,7 +102,7 @@ __device__ __forceinline__ bool pf_find_tile(const int32_t* __restrict__ offsets
     run += v;
   }
   __syncthreads();
-  int L = blockIdx.x, k = 0;
+  int L = pf_item_of_block(blockIdx.x, gridDim.x, xcd_run), k = 0;
   for (; k < 4; ++k) {
     const int n = pf_field(total, k) * NT;
     if (L < n) break;
