@@ -3,11 +3,11 @@
 
 A step is one whole layer call -- router top-K, permutation, expert FFN
 (gate_up + SiLU + down, routed experts and the shared expert) and combine,
-through moe_route_permute and moe_expert_ffn_combine (for decode batches one
-and two kernels: the top-K and permutation share a block, the combine runs in
-the down kernel's tail) -- over one batch of synthetic tokens already
-resident in HBM.  The same step through the four separate entry points is
-timed beside it (us_unfused).
+through moe_layer (for decode batches three kernels: every block of the
+gate_up kernel routes and permutes the batch itself, then down, then the
+combine) -- over one batch of synthetic tokens already resident in HBM.  The
+same step through the four separate entry points is timed beside it
+(us_unfused).
 
 Headline workload: the decode/verify layer at T=8 rows (H=2048, 512 experts
 top-10 plus one shared expert, I=512).  Every step uses the next of NBANKS
@@ -102,8 +102,8 @@ class LayerRunner:
                      torch.empty(G + 1, dtype=i32, device=dev))
         self.ws_p = torch.empty(max(1, moe.workspace_bytes(1, T, E, K, 0, 0, hs)), dtype=torch.uint8,
                                 device=dev)
-        self.ws_f = torch.empty(moe.workspace_bytes(3, T, E, K, H, wl.I, hs, act_mode),
-                                dtype=torch.uint8, device=dev)   # enough for either path
+        self.ws_f = torch.empty(moe.workspace_bytes(4, T, E, K, H, wl.I, hs, act_mode),
+                                dtype=torch.uint8, device=dev)   # enough for every path
         self.y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.distinct = []
@@ -112,12 +112,9 @@ class LayerRunner:
         moe = self.moe
         W = self.banks[step % len(self.banks)]
         lg = self.logits[step % len(self.logits)]
-        if self.fused:   # moe_route_permute + moe_expert_ffn_combine: the same results
-            moe.moe_route_permute(lg, self.wl.K, self.wl.has_shared, self.ws_p,
-                                  (self.ids, self.w) + self.perm)
-            moe.moe_expert_ffn_combine(W, self.x, self.wl.K, self.perm[1], self.perm[2],
-                                       self.perm[4], self.w, self.perm[3], self.act_mode,
-                                       ws=self.ws_f, y_slots=self.y, out=self.out)
+        if self.fused:   # the one-call layer (moe_layer): the same results
+            moe.moe_layer(W, self.x, lg, self.wl.K, self.act_mode, fused=True, ws=self.ws_f,
+                          perm=(self.ids, self.w) + self.perm, y_slots=self.y, out=self.out)
             return
         moe.moe_route_topk(lg, self.wl.K, self.ids, self.w)
         moe.moe_permute(self.ids, self.wl.E, self.wl.has_shared, self.ws_p, self.perm)
@@ -496,8 +493,9 @@ def main():
         "layer": {"us": round(head["ms_per_step"] * 1e3, 2), "us_eager": round(head["ms_eager"] * 1e3, 2),
                   "us_unfused": round(head["ms_unfused"] * 1e3, 2),
                   "timing": "HIP graph replay of the timed steps (eager time: us_eager); the step "
-                            "is moe_route_permute + moe_expert_ffn_combine (us_unfused: the four "
-                            "separate entry points, same results)",
+                            "is moe_layer, one call (us_unfused: the four separate entry points, "
+                            "same results); in moe_layer the dec_gate_up launch also routes and "
+                            "permutes the batch",
                   "GBs": round(head["layer_GBs"], 1),
                   "frac": round(head["layer_GBs"] / HBM_PEAK_GBS, 4),
                   "active_groups": round(head["active_groups"], 2),

@@ -23,6 +23,7 @@ MOE_ACT_FP8_SHARED = 3
 MOE_OP_PERMUTE = 1
 MOE_OP_EXPERT_FFN = 2
 MOE_OP_EXPERT_FFN_COMBINE = 3
+MOE_OP_LAYER = 4
 MOE_NOALLOC_WS_BYTES = 32 << 20
 
 
@@ -77,6 +78,8 @@ _SIGS = {
     "moe_expert_ffn_combine": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _I, _I, _P, _P, _P, _I,
                                     _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine_gated": (_I, [_P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_layer": (_I, [ctypes.POINTER(MoeNvfp4Weights), _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                       _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_router_topk": (_I, [ctypes.POINTER(MoeNvfp4Router), _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_timing_enable": (_I, [_I]),
     "moe_timing_reset": (_I, []),

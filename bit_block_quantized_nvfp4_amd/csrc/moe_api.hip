@@ -172,6 +172,10 @@ size_t moe_workspace_bytes(int op, int T, int E, int K, int H, int I, int has_sh
                            int act_mode) {
   if (!sizes_ok_common(T, E, K) || (has_shared != 0 && has_shared != 1)) return 0;
   if (op == MOE_OP_PERMUTE) return moe::permute_workspace_bytes(T, E, K);
+  if (op == MOE_OP_LAYER) {
+    if (H <= 0 || I <= 0 || act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED) return 0;
+    return moe::layer_workspace_bytes(T, E, K, H, I, has_shared, act_mode);
+  }
   if (op == MOE_OP_EXPERT_FFN || op == MOE_OP_EXPERT_FFN_COMBINE) {
     if (H <= 0 || I <= 0 || act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED) return 0;
     return op == MOE_OP_EXPERT_FFN ? moe::ffn_workspace_bytes(T, K, H, I, has_shared, act_mode)
@@ -305,6 +309,34 @@ int moe_expert_ffn_combine(const moe_nvfp4_weights* W, const uint16_t* x, int T,
                                                 w, slot_pos, gate, y_slots, out, ws,
                                                 (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn_combine launch");
+}
+
+int moe_layer(const moe_nvfp4_weights* W, const float* logits, const uint16_t* x, int T, int K,
+              int act_mode, const float* gate, int32_t* ids, float* w, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups,
+              uint16_t* y_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !logits || !x || !ids || !w || !counts || !offsets || !sorted_slot || !slot_pos ||
+      !groups || !y_slots || !out)
+    return fail(MOE_EINVAL, "moe_layer: null pointer");
+  if (!W->gu_codes || !W->gu_scales || !W->dn_codes || !W->dn_scales || !W->scale2)
+    return fail(MOE_EINVAL, "moe_layer: null weight pointer");
+  if (act_mode < MOE_ACT_BF16 || act_mode > MOE_ACT_FP8_SHARED)
+    return fail(MOE_EUNSUPPORTED, "moe_layer: unknown act_mode %d", act_mode);
+  if (!sizes_ok_common(T, W->E, K) || (W->has_shared != 0 && W->has_shared != 1))
+    return fail(MOE_EINVAL, "moe_layer: need T >= 1, 1 <= K <= min(E, 32), E <= 1024, has_shared in {0,1}");
+  if (W->H < 256 || W->H > 4096 || W->H % 256 != 0 || W->I < 128 || W->I > 1024 || W->I % 128 != 0)
+    return fail(MOE_EINVAL, "moe_layer: need H a multiple of 256 in [256, 4096] and I a multiple of 128 in [128, 1024] (H=%d I=%d)", W->H, W->I);
+  if (gate && !W->has_shared)
+    return fail(MOE_EINVAL, "moe_layer: a shared-expert gate needs has_shared");
+  const size_t need = moe::layer_workspace_bytes(T, W->E, K, W->H, W->I, W->has_shared, act_mode);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "moe_layer: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  int rc = ensure_init();
+  if (rc != MOE_OK) return rc;
+  const moe::RpOut ro{ids, w, counts, offsets, sorted_slot, slot_pos, groups};
+  hipError_t e = moe::launch_layer(*W, logits, x, T, K, act_mode, gate, ro, y_slots, out, ws,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_layer launch");
 }
 
 int moe_combine(const uint16_t* y_slots, const float* w, const int32_t* slot_pos, int T, int K,

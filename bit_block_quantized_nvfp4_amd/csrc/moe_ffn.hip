@@ -107,4 +107,41 @@ hipError_t launch_expert_ffn_combine(const moe_nvfp4_weights& W, const uint16_t*
   return launch_combine(y_slots, w, slot_pos, gate, T, K, W.H, W.has_shared ? 1 : 0, out, s);
 }
 
+// The whole layer in one call.  Decode batches of the bf16 or FP8 row arm
+// run three kernels (routing + permutation + gate_up, down, combine); other
+// calls run route+permute, then the expert FFN and the combine.  The
+// workspace serves the permutation first and the FFN after it (stream order).
+size_t layer_workspace_bytes(int T, int E, int K, int H, int I, int has_shared, int act_mode) {
+  const size_t a = permute_workspace_bytes(T, E, K);
+  const size_t b = ffn_combine_workspace_bytes(T, K, H, I, has_shared, act_mode);
+  return a > b ? a : b;
+}
+
+hipError_t launch_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x, int T,
+                        int K, int act_mode, const float* gate, const RpOut& ro,
+                        uint16_t* y_slots, uint16_t* out, void* ws, hipStream_t s) {
+  const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
+  if (decode_layer_supported(T, E, K, H, I, act_mode)) {
+    const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
+    uint8_t* wp = (uint8_t*)ws;
+    uint16_t* hbuf = (uint16_t*)wp;
+    wp += align256(S * I * sizeof(uint16_t));
+    uint8_t* xq = nullptr;
+    float* xs = nullptr;
+    if (act_mode != MOE_ACT_BF16) {
+      xq = wp;
+      wp += align256((size_t)T * H);
+      xs = (float*)wp;
+    }
+    hipError_t e = launch_decode_layer(W, logits, x, T, K, act_mode, ro, hbuf, xq, xs, y_slots, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(y_slots, ro.w, ro.slot_pos, gate, T, K, H, hs, out, s);
+  }
+  hipError_t e = launch_route_permute(logits, T, E, K, hs, ro.ids, ro.w, ro.counts, ro.offsets,
+                                      ro.sorted_slot, ro.slot_pos, ro.groups, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_ffn_combine(W, x, T, K, ro.offsets, ro.sorted_slot, ro.groups, act_mode,
+                                   ro.w, ro.slot_pos, gate, y_slots, out, ws, s);
+}
+
 }  // namespace moe

@@ -43,6 +43,7 @@
 
 #include "moe_ffn_common.hpp"
 #include "moe_internal.hpp"
+#include "moe_route_permute.hpp"
 
 namespace moe {
 
@@ -208,6 +209,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // there is the h rows issued ahead of the weights).
 constexpr int kGuPipe = 2;
 constexpr int kDnPipe = 2;
+// Chunks in flight per wave of the decode layer kernel when its blocks hold
+// only a few units (a wave then streams a whole unit alone).
+constexpr int kGuPipeFew = 8;
 
 // Activation rows -> f16 MFMA operand in LDS, in place (the rule of
 // k_dec_xprep, bit for bit): wave wv of WPB converts rows wv, wv + WPB, ...
@@ -513,6 +517,12 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(3))) v
 // and epilogue, so the same bits).  All units of a block read one activation
 // form, so the per-class FP8 arms keep k_dec_gate_up.
 constexpr int kGuCuWaves = 16;
+// LDS bytes per wave of the decode layer kernel: the unit's two scale runs
+// (16 rows x H/16 bytes each) and, with split K, at least the partial sums of
+// the wave's 16 x 32 outputs (2 KB).
+constexpr int dec_layer_slot_bytes(int nch, int ks) {
+  return ks > 1 && 256 * nch < 2048 ? 2048 : 256 * nch;
+}
 
 template <int NCH, int TR, bool FP8>
 __global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_gate_up_cu(
@@ -650,6 +660,199 @@ __global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_gate_up_cu(
     begin_unit(uu);
     wait_vmcnt<2 * D>();
     compute_unit();
+  }
+}
+
+// The decode layer's first kernel: router top-K and permutation of the batch
+// folded into the whole-CU gate_up (moe_layer).  Every block routes and
+// permutes the T <= 8 tokens itself in LDS (a few microseconds of latency,
+// the same in every block) instead of waiting for a separate launch; block 0
+// also writes the permutation's outputs, which the down and combine kernels
+// read after this kernel.  Meanwhile waves 8.. each stage one activation row
+// by DMA and convert it, with no barrier (each converts what it loaded).
+// Then the block takes its share of the active units as k_dec_gate_up_cu
+// does, with the group metadata from LDS.  Same arithmetic as the separate
+// launches, so the same bits (with KS > 1, the same bits as k_dec_gate_up's
+// split of the same KS).
+// DP: code chunks in flight per wave (kGuPipe, or kGuPipeFew when blocks hold
+// only a few units and the memory system would otherwise idle).
+// KS > 1 (split K, for launches whose blocks hold at most kGuCuWaves / KS
+// units): the block's waves work in rounds of kGuCuWaves / KS units, KS
+// consecutive waves per unit, each on NCH / KS consecutive chunks with the
+// unit's scale runs in its own LDS slot; waves 1 .. KS-1 of a unit leave their
+// partial sums in their slots, and after a barrier the unit's first wave adds
+// them in wave order (a fixed order: the result does not depend on timing)
+// and runs the epilogue.  Every wave takes part in every round's barriers.
+template <int NCH, int TR, bool FP8, int MAXV, int KS, int DP>
+__global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_layer_gate_up(
+    const float* __restrict__ logits, int E, const uint8_t* __restrict__ gu_codes,
+    const uint8_t* __restrict__ gu_scales, const float* __restrict__ scale2,
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs, int T,
+    int K, int H, int I, int has_shared, RpOut ro, uint16_t* __restrict__ h) {
+  constexpr int WPB = kGuCuWaves;
+  static_assert(WPB >= 8 + TR, "a converting wave per activation row");
+  static_assert(NCH % KS == 0 && WPB % KS == 0, "whole chunks per wave, whole units per round");
+  __shared__ RpLds L;
+  extern __shared__ __align__(16) _Float16 xl[];
+  constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
+  constexpr int SRUN = 128 * NCH;                   // scale bytes of 16 rows
+  constexpr int NCK = NCH / KS;                     // chunks per wave
+  constexpr int D = NCK < DP ? NCK : DP;
+  constexpr int SLOT = dec_layer_slot_bytes(NCH, KS);
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = wv % KS, c0 = ks * NCK;            // this wave's part of K
+  const bool blk0 = blockIdx.x == 0;
+  float* fac = (float*)((uint8_t*)xl + (size_t)TR * H * 2);
+  uint8_t* const slot0 = (uint8_t*)xl + (size_t)TR * H * 2 + 256;
+  uint8_t* sl = slot0 + (size_t)wv * SLOT;
+
+  // (1) waves 8 .. 8 + TR - 1: activation row wv - 8 -> LDS (chunk-swizzled),
+  // then converted in place by the same wave
+  if (wv >= 8 && wv - 8 < TR) {
+    const int r = wv - 8;
+    const uint16_t* xr_g = x + (size_t)(r < T ? r : T - 1) * H;
+    for (int base = 0; base < CPR; base += 64) {
+      const int ch = base + lane;
+      if (ch < CPR)
+        dma16(xr_g + 8 * (ch ^ (r & 15)), (uint8_t*)xl + 16 * ((size_t)r * CPR + base));
+    }
+    wait_vmcnt<0>();
+    dec_convert_rows<CPR, TR, 8>(xl, fac, xs, xq, H, T, FP8, FP8 && blk0, r, lane);
+  }
+  // (2) waves < T route; (3) the block permutes (barriers inside, which also
+  // publish the converted rows)
+  rp_route<MAXV, 64 * WPB>(logits, T, E, K, has_shared, blk0, ro, L);
+  const int nact = rp_permute<64 * WPB>(T, E, K, has_shared, blk0, ro, L);
+
+  // (4) this block's share of the active units
+  const int nbk = I / 16;
+  const int units = nact * nbk;
+  const int u0 = (int)((long long)blockIdx.x * units / gridDim.x);
+  const int u1 = (int)((long long)(blockIdx.x + 1) * units / gridDim.x);
+  const size_t rowb = (size_t)H / 2;
+  int e = 0, pb = 0, p0 = 0, n = 1, slot_l = 0;
+  float s2g = 0.f, s2u = 0.f;
+  const uint8_t* cg = gu_codes;
+  const uint8_t* cu = gu_codes;
+  u32x4 wg[NCK], wu[NCK];
+  auto issue = [&](int c) {
+    wg[c] = *(const u32x4*)(cg + 64 * c);
+    wu[c] = *(const u32x4*)(cu + 64 * c);
+  };
+  auto begin_unit = [&](int uu) {
+    const int a = uu / nbk;
+    pb = uu % nbk;
+    e = __builtin_amdgcn_readfirstlane(L.gl[a]);
+    const size_t grow = (size_t)e * 2 * I + (size_t)pb * 16;  // first gate row of the unit
+    const uint8_t* sg = gu_scales + grow * (H / 16);
+    dma_run<SRUN>(sg, sl, lane);
+    dma_run<SRUN>(sg + (size_t)I * (H / 16), sl + SRUN, lane);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    p0 = __builtin_amdgcn_readfirstlane(L.run[e] & 0xFFFF);
+    n = __builtin_amdgcn_readfirstlane(L.cnt[e]);
+    s2g = scale2[3 * e + 0];
+    s2u = scale2[3 * e + 1];
+    slot_l = L.ss_l[p0 + (lane < n ? lane : n - 1)];
+    cg = gu_codes + (grow + r16) * rowb + 16 * q + 64 * c0;
+    cu = cg + (size_t)I * rowb;
+#pragma unroll
+    for (int c = 0; c < D; ++c) issue(c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  float ums[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ums[t] = fac[t < TR ? t : TR - 1];
+  const int xr = r16 < T ? r16 : T - 1;
+  const uint8_t* xrow = (const uint8_t*)xl;
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q + 8 * c0;
+  // the swizzle touches only the low 4 bits of the chunk index, so the
+  // operand of sub-MFMA (c, j) sits at aoff[j] + 256 c
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = swz_off(xr, 4 * q + j, CPR) + 256 * c0;
+  // the MFMAs of this wave's chunks (chunk c once it has landed, then chunk
+  // c + D is issued); the scale runs must have landed
+  auto mma_unit = [&](f32x4& dg, f32x4& du) {
+    static_for<0, NCK>([&](auto ct) {
+      constexpr int c = decltype(ct)::value;
+      constexpr int issued = D + c < NCK ? D + c : NCK;
+      wait_vmcnt<2 * (issued - c - 1)>();
+      const f16x2 sgv = e4m3x2_to_f16(*(const uint16_t*)(srow + 8 * c));
+      const f16x2 suv = e4m3x2_to_f16(*(const uint16_t*)(srow + SRUN + 8 * c));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 av = *(const f16x8*)(xrow + aoff[j] + 256 * c);
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wg[c][j], j < 2 ? sgv.x : sgv.y), dg, 0, 0, 0);
+        du = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wu[c][j], j < 2 ? suv.x : suv.y), du, 0, 0, 0);
+      }
+      if constexpr (c + D < NCK) issue(c + D);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto epilogue = [&](const f32x4& dg, const f32x4& du) {
+    uint16_t hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float um = q == 0 ? ums[i] : (q == 1 ? ums[4 + i] : 0.f);  // tokens >= 8 are never stored
+      const float g = dg[i] * um * s2g, u = du[i] * um * s2u;
+      hv[i] = f32_to_bf16_bits(silu_f32(g) * u);
+    }
+    const int tokl = slot_token(slot_l, T, K, has_shared);
+    const int j = pb * 16 + r16;
+    for (int p = 0; p < n; ++p) {
+      const int tok = p < 64 ? __shfl(tokl, p, 64) : slot_token(L.ss_l[p0 + p], T, K, has_shared);
+      if (tok >= 0 && (tok >> 2) == q) {
+        const int i = tok & 3;
+        h[(size_t)(p0 + p) * I + j] = i == 0 ? hv[0] : (i == 1 ? hv[1] : (i == 2 ? hv[2] : hv[3]));
+      }
+    }
+  };
+  if constexpr (KS == 1) {
+    for (int uu = u0 + wv; uu < u1; uu += WPB) {  // uniform per wave; no barrier follows
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+      begin_unit(uu);
+      wait_vmcnt<2 * D>();  // the scale runs have landed
+      f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+      mma_unit(dg, du);
+      epilogue(dg, du);
+    }
+  } else {
+    constexpr int UPR = WPB / KS;                  // units per round
+    const int rounds = (u1 - u0 + UPR - 1) / UPR;  // uniform per block
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int uu = u0 + rd * UPR + wv / KS;
+      const bool has = uu < u1;                    // uniform per wave
+      if (rd > 0) __syncthreads();                 // the last round's partial sums are read
+      f32x4 dg = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+      if (has) {
+        begin_unit(uu);
+        wait_vmcnt<2 * D>();
+        mma_unit(dg, du);
+        if (ks > 0) {  // partial sums -> this wave's slot ([8][64] floats, lane fastest)
+          float* dst = (float*)sl + lane;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[64 * i] = dg[i];
+            dst[64 * (4 + i)] = du[i];
+          }
+        }
+      }
+      __syncthreads();
+      if (has && ks == 0) {
+#pragma unroll
+        for (int w = 1; w < KS; ++w) {
+          const float* src = (const float*)(sl + (size_t)w * SLOT) + lane;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dg[i] += src[64 * i];
+            du[i] += src[64 * (4 + i)];
+          }
+        }
+        epilogue(dg, du);
+      }
+    }
   }
 }
 
@@ -843,6 +1046,25 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 
 // --------------------------------- host -----------------------------------
 
+// The decode layer kernel's variants of one (NCH, TR, MAXV): K split over 1,
+// 2, 4 or 8 waves (where NCH allows), and without the split, the two pipeline
+// depths.
+template <int NCH, int TR, int MV, int KS, int DP>
+static void reg_dec_layer_gate_up1(std::vector<const void*>& k) {
+  if constexpr (NCH % KS == 0) {
+    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, false, MV, KS, DP>);
+    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, true, MV, KS, DP>);
+  }
+}
+template <int NCH, int TR, int MV>
+static void reg_dec_layer_gate_up(std::vector<const void*>& k) {
+  reg_dec_layer_gate_up1<NCH, TR, MV, 1, kGuPipe>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 1, kGuPipeFew>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 2, kGuPipeFew>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 4, kGuPipeFew>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 8, kGuPipeFew>(k);
+}
+
 void register_decode_kernels(std::vector<const void*>& k) {
   k.push_back((const void*)&k_dec_xprep<false>);
   k.push_back((const void*)&k_dec_xprep<true>);
@@ -878,6 +1100,20 @@ void register_decode_kernels(std::vector<const void*>& k) {
   MOE_REG_GUC(16)
 #undef MOE_REG_GUC
 #undef MOE_REG_GUC2
+#define MOE_REG_LGU2(NCH, TR)                \
+  reg_dec_layer_gate_up<NCH, TR, 8>(k); \
+  reg_dec_layer_gate_up<NCH, TR, 16>(k);
+#define MOE_REG_LGU(NCH) \
+  MOE_REG_LGU2(NCH, 1)   \
+  MOE_REG_LGU2(NCH, 2)   \
+  MOE_REG_LGU2(NCH, 4)   \
+  MOE_REG_LGU2(NCH, 8)
+  MOE_REG_LGU(2)
+  MOE_REG_LGU(4)
+  MOE_REG_LGU(8)
+  MOE_REG_LGU(16)
+#undef MOE_REG_LGU
+#undef MOE_REG_LGU2
 #undef MOE_REG_GU
 #undef MOE_REG_GU2
 #undef MOE_REG_GU3
@@ -951,6 +1187,16 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
 
 // Split K below this many gate_up units per CU (see k_dec_gate_up).
 constexpr long kGuSplitBelow = 2;
+// The decode layer kernel keeps kGuPipeFew chunks in flight per wave below
+// this many gate_up units per CU (a wave then streams its whole unit alone).
+constexpr long kLayerDeepBelow = 4;
+// K split of the decode layer kernel: at most kLayerSplitMaxKs waves per
+// unit, and only while a block holds at most kLayerSplitMaxShare units.
+// Measured at H = 2048, I = 512, E = 512, K = 10 (whole layer, weights cold):
+// T = 1 23.8 -> 22.3 us (8 waves), T = 2 26.6 -> 25.8, T = 3 29.5 -> 29.1
+// (4 waves); T = 4 33.4 / 33.5 and T = 6 41.4 / 42.1 with 2 waves.
+constexpr long kLayerSplitMaxKs = 8;
+constexpr long kLayerSplitMaxShare = 4;
 // Whole-CU gate_up blocks (k_dec_gate_up_cu) from this many units per CU on.
 constexpr long kGuCuFrom = 4;
 
@@ -1010,37 +1256,13 @@ static void launch_gu_pick(bool split, int wpb, bool cu_mode, const moe_nvfp4_we
                                   hbuf, dim3((unsigned)units), s);
 }
 
-hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
-                             const int32_t* offsets, const int32_t* sorted_slot,
-                             const int32_t* groups, int act_mode, uint16_t* hbuf, uint8_t* xq,
-                             float* xs, uint16_t* y, hipStream_t s) {
-  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
-  const int G = W.E + hs;
-  const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
-  // gate_up waves (units) per block: 4 (one staged copy of the activation
-  // rows per 4 units) once the units are plentiful, else 1 so that small T
-  // still spreads over many CUs (measured at H=2048, I=512, 256 CUs: 4 gains
-  // from about 2 units per CU on, T=3: 15.8 vs 17.8 us, T=6: 22.3 vs 37 us);
-  // fewer than kGuSplitBelow units per CU: one unit per block with K split
-  // over 4 waves (H a multiple of 512).
-  const long gu_units = (long)gmax * (I / 16), dn_units = (long)gmax * (H / 64);
+// The down launch of a decode FFN whose active groups number at most gmax.
+static hipError_t launch_dec_down_all(const moe_nvfp4_weights& W, int gmax, const int32_t* offsets,
+                                      const int32_t* groups, uint16_t* hbuf, uint16_t* y,
+                                      hipStream_t s) {
+  const int H = W.H, I = W.I;
+  const long dn_units = (long)gmax * (H / 64);
   const long cus = num_cus();
-  const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
-  const bool split = gu_units < kGuSplitBelow * cus && (H / 128) % 4 == 0;
-  // whole-CU blocks once every CU gets several units (one activation form
-  // per block: the bf16 arm or the FP8 row arm)
-  const bool cu_mode = !split && gu_units >= kGuCuFrom * cus &&
-                       (act_mode == MOE_ACT_BF16 || act_mode == MOE_ACT_FP8_ROW);
-  const int nch = H / 128;
-#define MOE_DEC_GU(NCH)                                                                             \
-  launch_gu_pick<NCH>(split, wpb_g, cu_mode, W, x, T, K, offsets, sorted_slot, groups, act_mode, \
-                      xq, xs, hbuf, gu_units, s)
-  if (nch == 2) MOE_DEC_GU(2);
-  else if (nch == 4) MOE_DEC_GU(4);
-  else if (nch == 8) MOE_DEC_GU(8);
-  else if (nch == 16) MOE_DEC_GU(16);
-  else return hipErrorInvalidValue;
-#undef MOE_DEC_GU
   // Down rows per wave: 64 (4 MFMA blocks) once that gives kDnWavesPerCu
   // waves per CU, else 32 or 16 (more, shorter units at small T).
   // (A block is 4 waves = 64 NB rows of one group either way.)
@@ -1068,6 +1290,117 @@ hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int 
 #undef MOE_DEC_DN2
 #undef MOE_DEC_DN
   return hipGetLastError();
+}
+
+hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
+                             const int32_t* offsets, const int32_t* sorted_slot,
+                             const int32_t* groups, int act_mode, uint16_t* hbuf, uint8_t* xq,
+                             float* xs, uint16_t* y, hipStream_t s) {
+  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
+  const int G = W.E + hs;
+  const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
+  // gate_up waves (units) per block: 4 (one staged copy of the activation
+  // rows per 4 units) once the units are plentiful, else 1 so that small T
+  // still spreads over many CUs (measured at H=2048, I=512, 256 CUs: 4 gains
+  // from about 2 units per CU on, T=3: 15.8 vs 17.8 us, T=6: 22.3 vs 37 us);
+  // fewer than kGuSplitBelow units per CU: one unit per block with K split
+  // over 4 waves (H a multiple of 512).
+  const long gu_units = (long)gmax * (I / 16);
+  const long cus = num_cus();
+  const int wpb_g = gu_units >= 2 * cus ? 4 : 1;
+  const bool split = gu_units < kGuSplitBelow * cus && (H / 128) % 4 == 0;
+  // whole-CU blocks once every CU gets several units (one activation form
+  // per block: the bf16 arm or the FP8 row arm)
+  const bool cu_mode = !split && gu_units >= kGuCuFrom * cus &&
+                       (act_mode == MOE_ACT_BF16 || act_mode == MOE_ACT_FP8_ROW);
+  const int nch = H / 128;
+#define MOE_DEC_GU(NCH)                                                                             \
+  launch_gu_pick<NCH>(split, wpb_g, cu_mode, W, x, T, K, offsets, sorted_slot, groups, act_mode, \
+                      xq, xs, hbuf, gu_units, s)
+  if (nch == 2) MOE_DEC_GU(2);
+  else if (nch == 4) MOE_DEC_GU(4);
+  else if (nch == 8) MOE_DEC_GU(8);
+  else if (nch == 16) MOE_DEC_GU(16);
+  else return hipErrorInvalidValue;
+#undef MOE_DEC_GU
+  return launch_dec_down_all(W, gmax, offsets, groups, hbuf, y, s);
+}
+
+bool decode_layer_supported(int T, int E, int K, int H, int I, int act_mode) {
+  return T >= 1 && T <= kRouteFuseMaxT && E <= kRpMaxE && K <= 32 && decode_supported(H, I) &&
+         (act_mode == MOE_ACT_BF16 || act_mode == MOE_ACT_FP8_ROW);
+}
+
+// The decode layer kernel for one (NCH, TR, FP8, MAXV): the K split `ks` and,
+// without a split, the pipeline depth.
+template <int NCH, int TR, bool F8, int MV>
+static void launch_dec_layer_gu(int ks, bool deep, const moe_nvfp4_weights& W, const float* logits,
+                                const uint16_t* x, int T, int K, const RpOut& ro, uint16_t* hbuf,
+                                uint8_t* xq, float* xs, hipStream_t s) {
+  const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
+  const dim3 grid((unsigned)num_cus()), block(64 * kGuCuWaves);
+  const size_t lds = (size_t)TR * H * 2 + 256 + (size_t)kGuCuWaves * dec_layer_slot_bytes(NCH, ks);
+#define MOE_DEC_LGU0(KS, DP)                                                                     \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_layer_gate_up<NCH, TR, F8, MV, KS, DP>), grid, block, lds, \
+             s, logits, E, W.gu_codes, W.gu_scales, W.scale2, x, xq, xs, T, K, H, I, hs, ro, hbuf)
+  if constexpr (NCH % 8 == 0) {
+    if (ks == 8) { MOE_DEC_LGU0(8, kGuPipeFew); return; }
+  }
+  if constexpr (NCH % 4 == 0) {
+    if (ks == 4) { MOE_DEC_LGU0(4, kGuPipeFew); return; }
+  }
+  if (ks == 2) MOE_DEC_LGU0(2, kGuPipeFew);
+  else if (deep) MOE_DEC_LGU0(1, kGuPipeFew);
+  else MOE_DEC_LGU0(1, kGuPipe);
+#undef MOE_DEC_LGU0
+}
+
+// One block per CU: routing + permutation + gate_up (k_dec_layer_gate_up),
+// then the down launch.  When a block's share of units is at most
+// kLayerSplitMaxShare, the K split is the largest of 8, 4, 2 (dividing
+// H / 128, at most kLayerSplitMaxKs) whose waves cover every unit of the
+// share in one round; the share is bounded with the most groups the batch
+// can activate, min(T K, E) (+ the shared expert).
+hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x,
+                               int T, int K, int act_mode, const RpOut& ro, uint16_t* hbuf,
+                               uint8_t* xq, float* xs, uint16_t* y, hipStream_t s) {
+  const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
+  const int G = E + hs;
+  const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
+  const bool fp8 = act_mode != MOE_ACT_BF16;
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
+  const int nch = H / 128;
+  const long units = (long)gmax * (I / 16);
+  const long share = (units + num_cus() - 1) / num_cus();
+  int ks = 1;
+  if (share <= kLayerSplitMaxShare)
+    while (2 * ks <= kLayerSplitMaxKs && 2 * ks * share <= kGuCuWaves && nch % (2 * ks) == 0) ks *= 2;
+  const bool deep = units < kLayerDeepBelow * num_cus();
+#define MOE_DEC_LGU2(NCH, TR)                                                                     \
+  do {                                                                                            \
+    if (E <= 512) {                                                                               \
+      if (fp8) launch_dec_layer_gu<NCH, TR, true, 8>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);   \
+      else launch_dec_layer_gu<NCH, TR, false, 8>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);      \
+    } else {                                                                                      \
+      if (fp8) launch_dec_layer_gu<NCH, TR, true, 16>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);  \
+      else launch_dec_layer_gu<NCH, TR, false, 16>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);     \
+    }                                                                                             \
+  } while (0)
+#define MOE_DEC_LGU(NCH)                    \
+  do {                                      \
+    if (tr == 1) MOE_DEC_LGU2(NCH, 1);      \
+    else if (tr == 2) MOE_DEC_LGU2(NCH, 2); \
+    else if (tr == 4) MOE_DEC_LGU2(NCH, 4); \
+    else MOE_DEC_LGU2(NCH, 8);              \
+  } while (0)
+  if (nch == 2) MOE_DEC_LGU(2);
+  else if (nch == 4) MOE_DEC_LGU(4);
+  else if (nch == 8) MOE_DEC_LGU(8);
+  else if (nch == 16) MOE_DEC_LGU(16);
+  else return hipErrorInvalidValue;
+#undef MOE_DEC_LGU
+#undef MOE_DEC_LGU2
+  return launch_dec_down_all(W, gmax, ro.offsets, ro.groups, hbuf, y, s);
 }
 
 }  // namespace moe

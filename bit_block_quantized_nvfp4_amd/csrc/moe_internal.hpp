@@ -95,6 +95,29 @@ hipError_t launch_prefill_fused(const moe_nvfp4_weights& W, int T, int K, const 
                                 hipStream_t s);
 bool decode_supported(int H, int I);
 size_t xprep_workspace_bytes(int T, int H);
+// The permutation's global outputs (the layout of moe_route_permute).
+struct RpOut {
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slot;
+  int32_t* slot_pos;
+  int32_t* groups;
+};
+// The decode layer kernels (routing and permutation inside the gate_up
+// launch, then down): batches of up to kRouteFuseMaxT tokens, the bf16 and
+// the FP8 row arms, decode-supported H and I.
+bool decode_layer_supported(int T, int E, int K, int H, int I, int act_mode);
+hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x,
+                               int T, int K, int act_mode, const RpOut& ro, uint16_t* hbuf,
+                               uint8_t* xq, float* xs, uint16_t* y, hipStream_t s);
+// The whole layer (moe_layer): the decode layer kernels and the combine, or
+// route+permute and the expert FFN + combine.
+size_t layer_workspace_bytes(int T, int E, int K, int H, int I, int has_shared, int act_mode);
+hipError_t launch_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x, int T,
+                        int K, int act_mode, const float* gate, const RpOut& ro,
+                        uint16_t* y_slots, uint16_t* out, void* ws, hipStream_t s);
 hipError_t launch_decode_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
                              const int32_t* groups, int act_mode, uint16_t* hbuf, uint8_t* xq,

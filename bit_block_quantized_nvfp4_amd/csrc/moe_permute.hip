@@ -18,6 +18,7 @@
 // uses to find the expert of a work unit with one load.
 #include "moe_device.hpp"
 #include "moe_internal.hpp"
+#include "moe_route_permute.hpp"
 #include "moe_topk.hpp"
 
 namespace moe {
@@ -29,34 +30,6 @@ constexpr int kSmallSlots = 2048;
 constexpr int kMaxE = 1024;
 constexpr int kFuseBlock = 64 * kRouteFuseMaxT;  // one wave per token of the fused batch
 static_assert(kRouteFuseMaxT * 32 <= kFuseBlock, "one slot per thread in the fused permutation");
-
-// Exclusive scan, in place, of a[0..n) held in LDS, by a block of NT threads.
-// Returns the total.  Must be called by every thread of the block.
-template <int NT = kBlock>
-__device__ int block_exclusive_scan(int* a, int n, int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (n + NT - 1) / NT;
-  const int lo = min(tid * per, n), hi = min(lo + per, n);
-  int local = 0;
-  for (int i = lo; i < hi; ++i) local += a[i];
-  const int incl = wave_incl_scan(local, lane);
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    before += (i < wv) ? wsum[i] : 0;
-    total += wsum[i];
-  }
-  int run = before + incl - local;
-  for (int i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
-}
 
 // Ranks one chunk of up to 256 slots starting at c0 and scatters them; e is
 // the expert id of this thread's slot c0 + tid (ignored past TK).  run[e]
@@ -151,7 +124,7 @@ __device__ void permute_small_body(const int32_t* ids, int T, int E, int K, int 
   for (int e = tid; e < G; e += kBlock) counts[e] = run[e];
   write_groups(run, G, groups);
   __syncthreads();
-  const int total = block_exclusive_scan(run, G, wsum);
+  const int total = block_exclusive_scan<kBlock>(run, G, wsum);
   for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
   if (tid == 0) offsets[G] = total;
   const int off_shared = has_shared ? run[E] : 0;  // scatter_chunk only moves run[e < E]
@@ -176,74 +149,18 @@ __global__ __launch_bounds__(kBlock) void k_permute_small(
 }
 
 // Router top-K and permutation of a batch of up to kRouteFuseMaxT tokens in
-// one block of one wave per token: wave t routes token t (the router stage's
-// rule, moe_topk.hpp) and keeps its ids in LDS too; then the block permutes
-// the T*K <= kFuseBlock slots, one per thread.  Same outputs as the two
-// kernels, one launch fewer.
-//  * counts: LDS atomics; the shared group holds T;
-//  * one exclusive scan of count | (count > 0) << 16 gives both the group
-//    offsets (low 16 bits; at most kFuseBlock + kRouteFuseMaxT slots) and each
-//    non-empty group's index in the compact list (high bits);
-//  * the rank of slot s inside its group is the number of earlier slots with
-//    the same expert, counted from the ids in LDS (the stable counting sort of
-//    the multi-block path, without its per-chunk masks).
-// The logits loads are the first global accesses of the routing waves, so
-// their latency overlaps only the LDS set-up.
+// one block of one wave per token (moe_route_permute.hpp): same outputs as
+// the two kernels, one launch fewer.
 template <int MAXV>
 __global__ __launch_bounds__(kFuseBlock) void k_route_permute_small(
     const float* __restrict__ logits, int T, int E, int K, int has_shared,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ groups) {
-  __shared__ int cnt[kMaxE + 1];
-  __shared__ int run[kMaxE + 1];
-  __shared__ int wsum[kFuseBlock / 64];
-  __shared__ __align__(16) int32_t ids_l[kFuseBlock];
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int G = E + has_shared, TK = T * K;
-  for (int e = tid; e < G; e += kFuseBlock) cnt[e] = (e == E) ? T : 0;
-  if (wv < T)  // uniform per wave
-    route_row_topk<MAXV>(logits + (size_t)wv * E, E, K, ids + (size_t)wv * K, w + (size_t)wv * K,
-                         ids_l + wv * K);
-  __syncthreads();
-  const int e_s = tid < TK ? ids_l[tid] : -1;
-  const bool ok = e_s >= 0 && e_s < E;
-  if (ok) atomicAdd(&cnt[e_s], 1);
-  __syncthreads();
-  for (int e = tid; e < G; e += kFuseBlock) {
-    const int c = cnt[e];
-    counts[e] = c;
-    run[e] = c | ((c > 0 ? 1 : 0) << 16);
-  }
-  __syncthreads();
-  const int packed = block_exclusive_scan<kFuseBlock>(run, G, wsum);
-  const int nz = packed >> 16;
-  for (int e = tid; e < G; e += kFuseBlock) {
-    const int v = run[e];
-    offsets[e] = v & 0xFFFF;
-    if (cnt[e] > 0) groups[1 + (v >> 16)] = e;
-  }
-  for (int i = nz + tid; i < G; i += kFuseBlock) groups[1 + i] = -1;  // deterministic tail
-  if (tid == 0) {
-    offsets[G] = packed & 0xFFFF;
-    groups[0] = nz;
-  }
-  if (tid < TK) {
-    int pos = -1;
-    if (ok) {
-      int r = 0;
-      const int s4 = tid & ~3;
-      for (int j = 0; j < s4; j += 4) {
-        const int4 v = *(const int4*)(ids_l + j);
-        r += (v.x == e_s) + (v.y == e_s) + (v.z == e_s) + (v.w == e_s);
-      }
-      for (int j = s4; j < tid; ++j) r += ids_l[j] == e_s;
-      pos = (run[e_s] & 0xFFFF) + r;
-      sorted_slot[pos] = tid;
-    }
-    slot_pos[tid] = pos;
-  }
-  if (has_shared) write_shared_group(T, TK, run[E] & 0xFFFF, sorted_slot, slot_pos, tid, kFuseBlock);
+  __shared__ RpLds L;
+  const RpOut o{ids, w, counts, offsets, sorted_slot, slot_pos, groups};
+  rp_route<MAXV, kFuseBlock>(logits, T, E, K, has_shared, true, o, L);
+  rp_permute<kFuseBlock>(T, E, K, has_shared, true, o, L);
 }
 
 // Tile histograms, written expert-major: cnt[e * ntiles + tile].
@@ -276,7 +193,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_scan_tiles(int32_t* __restri
     const int i = b0 + tid;
     buf[tid] = (i < ntiles) ? row[i] : 0;
     __syncthreads();
-    const int sum = block_exclusive_scan(buf, kBlock, wsum);
+    const int sum = block_exclusive_scan<kBlock>(buf, kBlock, wsum);
     if (i < ntiles) row[i] = carry + buf[tid];
     carry += sum;
     __syncthreads();
@@ -303,7 +220,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_scatter(
     write_groups(run, G, groups);
   }
   __syncthreads();
-  const int total = block_exclusive_scan(run, G, wsum);
+  const int total = block_exclusive_scan<kBlock>(run, G, wsum);
   if (tile == 0) {
     for (int e = tid; e < G; e += kBlock) offsets[e] = run[e];
     if (tid == 0) offsets[G] = total;

@@ -15,7 +15,8 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_ACT_BF16, MOE_ACT_FP8_ROUTED, MOE_ACT_FP8_ROW, MOE_ACT_FP8_SHARED,
-                   MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_COMBINE, MOE_OP_PERMUTE, check)
+                   MOE_OP_EXPERT_FFN, MOE_OP_EXPERT_FFN_COMBINE, MOE_OP_LAYER, MOE_OP_PERMUTE,
+                   check)
 
 __all__ = [
     "NVFP4Weights", "moe_init", "moe_route_topk", "moe_permute", "moe_expert_ffn",
@@ -208,8 +209,7 @@ def moe_expert_ffn_combine(W: NVFP4Weights, x: torch.Tensor, K: int, offsets: to
                            gate: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                            y_slots: Optional[torch.Tensor] = None,
                            out: Optional[torch.Tensor] = None):
-    """Expert FFN + combine (the combine folded into the down kernel for
-    decode batches).  Returns (y_slots, out)."""
+    """moe_expert_ffn followed by the combine, one call.  Returns (y_slots, out)."""
     _need(x, torch.bfloat16, name="x")
     T, H = x.shape
     if H != W.H:
@@ -311,22 +311,63 @@ def moe_combine_gated(y_slots: torch.Tensor, w: torch.Tensor, slot_pos: torch.Te
 
 
 def moe_layer(W: NVFP4Weights, x: torch.Tensor, logits: torch.Tensor, K: int,
-              act_mode: int = MOE_ACT_BF16, fused: bool = False) -> dict:
+              act_mode: int = MOE_ACT_BF16, fused: bool = False,
+              gate: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+              perm=None, y_slots: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> dict:
     """One layer call: route -> permute -> expert FFN -> combine, all on the GPU.
-    fused=True uses moe_route_permute and moe_expert_ffn_combine (same results)."""
-    if fused:
-        ids, w, counts, offsets, sorted_slot, slot_pos, groups = moe_route_permute(
-            logits, K, W.has_shared)
-        y, out = moe_expert_ffn_combine(W, x, K, offsets, sorted_slot, groups, w, slot_pos,
-                                        act_mode)
+    fused=True is the C entry moe_layer (three kernels for decode batches; the
+    permutation's outputs in `perm` = (ids, w, counts, offsets, sorted_slot,
+    slot_pos, groups) when given); fused=False runs the four separate entry
+    points.  Both give the same results."""
+    if not fused:
+        ids, w = moe_route_topk(logits, K)
+        counts, offsets, sorted_slot, slot_pos, groups = moe_permute(ids, W.E, W.has_shared)
+        y = moe_expert_ffn(W, x, K, offsets, sorted_slot, groups, act_mode)
+        o = (moe_combine(y, w, slot_pos, K, W.has_shared) if gate is None
+             else moe_combine_gated(y, w, slot_pos, gate, K))
         return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,
-                    slot_pos=slot_pos, groups=groups, y_slots=y, out=out)
-    ids, w = moe_route_topk(logits, K)
-    counts, offsets, sorted_slot, slot_pos, groups = moe_permute(ids, W.E, W.has_shared)
-    y = moe_expert_ffn(W, x, K, offsets, sorted_slot, groups, act_mode)
-    out = moe_combine(y, w, slot_pos, K, W.has_shared)
+                    slot_pos=slot_pos, groups=groups, y_slots=y, out=o)
+    _need(logits, torch.float32, name="logits")
+    _need(x, torch.bfloat16, name="x")
+    T, E = logits.shape
+    H = x.shape[1]
+    if H != W.H or E != W.E or x.shape[0] != T:
+        raise ValueError("logits / x do not match the weight bank")
+    hs = W.has_shared
+    G = E + int(hs)
+    S = T * K + (T if hs else 0)
+    dev = x.device
+    i32 = torch.int32
+    if perm is None:
+        perm = (torch.empty((T, K), dtype=i32, device=dev),
+                torch.empty((T, K), dtype=torch.float32, device=dev),
+                torch.empty(G, dtype=i32, device=dev), torch.empty(G + 1, dtype=i32, device=dev),
+                torch.empty(S, dtype=i32, device=dev), torch.empty(S, dtype=i32, device=dev),
+                torch.empty(G + 1, dtype=i32, device=dev))
+    ids, w, counts, offsets, sorted_slot, slot_pos, groups = perm
+    _need(ids, i32, (T, K), "ids")
+    _need(w, torch.float32, (T, K), "w")
+    _need(counts, i32, (G,), "counts")
+    _need(offsets, i32, (G + 1,), "offsets")
+    _need(sorted_slot, i32, (S,), "sorted_slot")
+    _need(slot_pos, i32, (S,), "slot_pos")
+    _need(groups, i32, (G + 1,), "groups")
+    y_slots = torch.empty((S, H), dtype=torch.bfloat16, device=dev) if y_slots is None else y_slots
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    _need(y_slots, torch.bfloat16, (S, H), "y_slots")
+    _need(out, torch.bfloat16, (T, H), "out")
+    if gate is not None:
+        _need(gate, torch.float32, (T,), "gate")
+    nb = workspace_bytes(MOE_OP_LAYER, T, E, K, H, W.I, hs, act_mode)
+    ws = _workspace(nb, dev, ws)
+    st = W.struct()
+    check(_lib.lib().moe_layer(ctypes.byref(st), _ptr(logits), _ptr(x), T, K, act_mode, _ptr(gate),
+                               _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+                               _ptr(slot_pos), _ptr(groups), _ptr(y_slots), _ptr(out), _ptr(ws), nb,
+                               _stream()))
     return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted_slot=sorted_slot,
-                slot_pos=slot_pos, groups=groups, y_slots=y, out=out)
+                slot_pos=slot_pos, groups=groups, y_slots=y_slots, out=out)
 
 
 def timing_enable(on: bool = True) -> None:

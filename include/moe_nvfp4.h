@@ -69,6 +69,7 @@ extern "C" {
 #define MOE_OP_PERMUTE 1
 #define MOE_OP_EXPERT_FFN 2
 #define MOE_OP_EXPERT_FFN_COMBINE 3
+#define MOE_OP_LAYER 4
 
 /*
  * A bank of NVFP4 experts: E routed experts plus, if has_shared, one shared
@@ -281,6 +282,33 @@ int moe_expert_ffn_combine(const moe_nvfp4_weights* W, const uint16_t* x, int T,
                            const int32_t* groups, int act_mode, const float* w,
                            const int32_t* slot_pos, const float* gate, uint16_t* y_slots,
                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer in one call: moe_route_permute, then moe_expert_ffn_combine
+ * (the layer's stages in the order of the issue "[job] Qwen3.8-Flash-Next:
+ * long-context cold prefill to SGLang parity", section "Localising the
+ * remaining ~0.56 %": router top-k, the permutation, the routed and shared
+ * experts, the combine), with the same outputs bit for bit.  For decode
+ * batches (T <= 8, the bf16 or the FP8 row arm, H / 128 in {2, 4, 8, 16} and
+ * I / 128 in {1, 2, 4, 8}) it runs three kernels: every block of the gate_up
+ * kernel routes and permutes the batch itself in LDS, so the routing costs no
+ * launch of its own (the launch structure of the decode item A2 of the page
+ * "handover briefs": top-10 + shared in one launch per projection); other
+ * calls run the route+permute and the FFN + combine kernels.
+ *
+ *   logits [T][E] float32                           (in)  router scores
+ *   x, W, K, act_mode, gate                         (in)  as moe_expert_ffn_combine
+ *   ids, w, counts, offsets, sorted_slot, slot_pos, groups
+ *                                                   (out) as moe_route_permute
+ *   y_slots, out                                    (out) as moe_expert_ffn_combine
+ *   ws  at least moe_workspace_bytes(MOE_OP_LAYER, T, E, K, H, I, has_shared,
+ *       act_mode) bytes (it serves the permutation, then the FFN)
+ * Errors: those of the two calls, checked before anything is enqueued.
+ */
+int moe_layer(const moe_nvfp4_weights* W, const float* logits, const uint16_t* x, int T, int K,
+              int act_mode, const float* gate, int32_t* ids, float* w, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int32_t* groups,
+              uint16_t* y_slots, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

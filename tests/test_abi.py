@@ -20,7 +20,7 @@ def test_header_declares_the_four_layer_calls():
     names = declared_functions()
     for n in ("moe_route_topk", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_init",
               "moe_last_error", "moe_workspace_bytes", "moe_router_topk", "moe_combine_gated", "moe_route_permute",
-              "moe_expert_ffn_combine"):
+              "moe_expert_ffn_combine", "moe_layer"):
         assert n in names
 
 
@@ -75,6 +75,19 @@ def test_argument_errors_are_reported_without_a_gpu(lib):
     assert need >= lib.moe_workspace_bytes(L.MOE_OP_EXPERT_FFN, 4, 8, 2, 256, 128, 1, 0) > 0
     assert fc(ctypes.byref(Ws), one, 4, 2, one, one, one, 0, one, one, None, one, one, one, need - 1,
               None) == L.MOE_EWORKSPACE
+    ly = lib.moe_layer
+    nl = lib.moe_workspace_bytes(L.MOE_OP_LAYER, 4, 8, 2, 256, 128, 1, 0)
+    assert nl >= need
+    assert ly(ctypes.byref(Ws), None, one, 4, 2, 0, None, one, one, one, one, one, one, one, one,
+              one, one, nl, None) == L.MOE_EINVAL                                         # no logits
+    assert ly(ctypes.byref(Ws), one, one, 4, 2, 7, None, one, one, one, one, one, one, one, one,
+              one, one, nl, None) == L.MOE_EUNSUPPORTED                                   # act_mode
+    assert ly(ctypes.byref(W), one, one, 4, 2, 0, one, one, one, one, one, one, one, one, one,
+              one, one, nl, None) == L.MOE_EINVAL                                         # gate, no shared
+    assert ly(ctypes.byref(Ws), one, one, 4, 9, 0, None, one, one, one, one, one, one, one, one,
+              one, one, nl, None) == L.MOE_EINVAL                                         # K > E
+    assert ly(ctypes.byref(Ws), one, one, 4, 2, 0, None, one, one, one, one, one, one, one, one,
+              one, one, nl - 1, None) == L.MOE_EWORKSPACE
     rt = lib.moe_router_topk
     R = L.MoeNvfp4Router(16, 16, 1.0, 64, 512, 1)
     assert rt(ctypes.byref(R), one, 4, 2, one, one, one, None, None) == L.MOE_EINVAL   # gate row, no gate
@@ -102,4 +115,9 @@ def test_workspace_sizes(lib):
     fp8 = ws(L.MOE_OP_EXPERT_FFN, 4096, 512, 10, 2048, 512, 1, L.MOE_ACT_FP8_ROW)
     assert bf >= S * 512 * 2 and fp8 >= bf + 4096 * 2048 + 4096 * 4
     assert ws(L.MOE_OP_EXPERT_FFN, 4096, 512, 10, 2048, 512, 1, 9) == 0
+    # the layer's workspace serves the permutation, then the FFN + combine
+    for T in (8, 4096):
+        lay = ws(L.MOE_OP_LAYER, T, 512, 10, 2048, 512, 1, L.MOE_ACT_BF16)
+        assert lay >= ws(L.MOE_OP_PERMUTE, T, 512, 10, 0, 0, 1, 0)
+        assert lay >= ws(L.MOE_OP_EXPERT_FFN_COMBINE, T, 512, 10, 2048, 512, 1, L.MOE_ACT_BF16)
     assert ws(99, 4, 8, 2, 256, 128, 0, 0) == 0

@@ -148,9 +148,122 @@ def test_ffn_combine_no_active_group(moe):
     assert torch.count_nonzero(out).item() == 0
 
 
+def _gate_up_splits_k(wl):
+    """Whether moe_expert_ffn splits the decode gate_up K over 4 waves for this
+    launch (fewer than 2 gate_up units per CU, H / 128 a multiple of 4)."""
+    if wl.T > 8:
+        return False
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gmax = min(wl.T * wl.K + int(wl.has_shared), wl.E + int(wl.has_shared))
+    return gmax * (wl.I // 16) < 2 * cus and (wl.H // 128) % 4 == 0
+
+
+def _layer_split_k(wl, act_mode):
+    """The K split of moe_layer's gate_up (1 = none), or None when the call
+    takes the separate launches' path: when the largest possible block share
+    of gate_up units is at most 4, the largest of 8, 4, 2 dividing H / 128
+    whose waves (16 per CU) cover the share in one round."""
+    nch, ncd = wl.H // 128, wl.I // 128
+    if not (1 <= wl.T <= 8 and wl.E <= 1024 and wl.K <= 32 and act_mode in (0, 1)
+            and wl.H % 128 == 0 and wl.I % 128 == 0 and nch in (2, 4, 8, 16) and ncd in (1, 2, 4, 8)):
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gmax = min(wl.T * wl.K + int(wl.has_shared), wl.E + int(wl.has_shared))
+    share = -(-gmax * (wl.I // 16) // cus)
+    ks = 1
+    while share <= 4 and 2 * ks <= 8 and 2 * ks * share <= 16 and nch % (2 * ks) == 0:
+        ks *= 2
+    return ks
+
+
+def _same_sums(wl, act_mode):
+    """Whether the one-call layer and the separate launches add the gate_up
+    products in the same order (the same K split, or the same path), so their
+    outputs agree bit for bit."""
+    ks = _layer_split_k(wl, act_mode)
+    return ks is None or ks == (4 if _gate_up_splits_k(wl) else 1)
+
+
+def _layer_vs_calls(moe, wl, act_mode=0, gate=None):
+    W = moe.NVFP4Weights.from_bank(wl.weights)
+    x = x_dev(wl.x_bf16)
+    lg = torch.from_numpy(wl.logits).cuda()
+    one = moe.moe_layer(W, x, lg, wl.K, act_mode, fused=True, gate=gate)
+    again = moe.moe_layer(W, x, lg, wl.K, act_mode, fused=True, gate=gate)
+    perm = moe.moe_route_permute(lg, wl.K, wl.has_shared)
+    ids, w, counts, offsets, sorted_slot, slot_pos, groups = perm
+    y_ref, out_ref = moe.moe_expert_ffn_combine(W, x, wl.K, offsets, sorted_slot, groups, w, slot_pos,
+                                                act_mode, gate=gate)
+    torch.cuda.synchronize()
+    names = ("ids", "w", "counts", "offsets", "sorted_slot", "slot_pos", "groups")
+    for nm, ref in zip(names, perm):
+        assert torch.equal(one[nm], ref), nm
+        assert torch.equal(again[nm], ref), nm
+    assert torch.equal(one["y_slots"].view(torch.int16), again["y_slots"].view(torch.int16))
+    assert torch.equal(one["out"].view(torch.int16), again["out"].view(torch.int16))
+    if _same_sums(wl, act_mode):
+        assert torch.equal(one["y_slots"].view(torch.int16), y_ref.view(torch.int16))
+        assert torch.equal(one["out"].view(torch.int16), out_ref.view(torch.int16))
+    else:  # another summation order: within a few bf16 roundings of each other
+        assert normwise(bf16_np(one["out"]), bf16_np(out_ref)) <= 8e-3
+    return one
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_layer_one_call_matches_the_calls(moe, T):
+    """moe_layer (routing and permutation inside the gate_up launch) against
+    moe_route_permute + moe_expert_ffn_combine, and the exact oracle."""
+    wl = workload_for("decode", T=T)
+    flush(f"moe_layer decode T={T}")
+    one = _layer_vs_calls(moe, wl)
+    exact = oracle.moe_layer(wl.x_bf16, wl.logits, wl.weights, wl.K)
+    assert normwise(bf16_np(one["out"]), exact["out"]) <= 2e-2
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=8, H=2048, E=1000, K=10, I=512, has_shared=True),   # E > 512: 16 logits per lane
+    dict(T=8, H=2048, E=1024, K=32, I=512, has_shared=False),  # the largest E and K
+    dict(T=5, H=2048, E=64, K=10, I=512, has_shared=True),
+    dict(T=8, H=256, E=4, K=2, I=128, has_shared=True),       # smallest H and I, few groups
+    dict(T=7, H=1024, E=16, K=4, I=1024, has_shared=False),
+    dict(T=3, H=512, E=16, K=4, I=256, has_shared=True),      # gate_up K split in the calls
+    dict(T=1, H=2048, E=512, K=1, I=512, has_shared=False),   # one slot
+    dict(T=7, H=4096, E=16, K=4, I=1024, has_shared=False),   # no decode kernels: the calls' path
+    dict(T=40, H=512, E=16, K=4, I=256, has_shared=True),     # T > 8: the calls' path
+])
+def test_layer_one_call_shapes(moe, cfg):
+    wl = make_workload("ly", seed=13, **cfg)
+    flush(f"moe_layer {cfg}")
+    _layer_vs_calls(moe, wl)
+
+
+def test_layer_one_call_arms_and_gate(moe):
+    wl = workload_for("decode", T=8)
+    g = torch.from_numpy(np.linspace(-3, 3, wl.T).astype(np.float32)).cuda()
+    for act_mode in (0, 1, 2, 3):   # 2 and 3 (per-class arms) take the calls' path
+        flush(f"moe_layer arms act_mode={act_mode}")
+        _layer_vs_calls(moe, wl, act_mode=act_mode)
+    _layer_vs_calls(moe, wl, act_mode=1, gate=g)
+    _layer_vs_calls(moe, wl, act_mode=0, gate=g)
+
+
+def test_layer_one_call_ties_and_invalid_rows(moe):
+    """All-equal, NaN and -inf logit rows: the layer's routing is the router
+    stage's rule in every block, and block 0 publishes it."""
+    wl = make_workload("lt", T=4, H=512, E=64, K=6, I=256, has_shared=True, seed=21)
+    lg = wl.logits.copy()
+    lg[0, :] = 0.0
+    lg[1, 5] = np.nan
+    lg[2, :] = -np.inf
+    lg[3, ::2] = np.inf
+    wl.logits = np.ascontiguousarray(lg)
+    _layer_vs_calls(moe, wl)
+
+
 @pytest.mark.parametrize("T", DECODE_TS)
 def test_fused_layer_against_oracle(moe, T):
-    """moe_layer(fused=True) through the same gates as the unfused layer."""
+    """moe_layer(fused=True), the one-call layer, through the same gates as the
+    unfused layer."""
     wl = workload_for("decode", T=T)
     W = moe.NVFP4Weights.from_bank(wl.weights)
     r = moe.moe_layer(W, x_dev(wl.x_bf16), torch.from_numpy(wl.logits).cuda(), wl.K, fused=True)
