@@ -50,7 +50,9 @@ NLOGITS = 16
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "expert_ffn_hbm_traffic_all_workloads.md")
 DECODE_SOURCES = ["bit_block_quantized_nvfp4_amd/csrc/moe_ffn_decode.hip",
                   "bit_block_quantized_nvfp4_amd/csrc/moe_ffn_common.hpp",
-                  "bit_block_quantized_nvfp4_amd/csrc/moe_device.hpp"]
+                  "bit_block_quantized_nvfp4_amd/csrc/moe_device.hpp",
+                  "bit_block_quantized_nvfp4_amd/csrc/moe_route_permute.hpp",
+                  "bit_block_quantized_nvfp4_amd/csrc/moe_topk.hpp"]
 
 
 def measured_traffic():

@@ -209,9 +209,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 // there is the h rows issued ahead of the weights).
 constexpr int kGuPipe = 2;
 constexpr int kDnPipe = 2;
-// Chunks in flight per wave of the decode layer kernel when its blocks hold
-// only a few units (a wave then streams a whole unit alone).
-constexpr int kGuPipeFew = 8;
 
 // Activation rows -> f16 MFMA operand in LDS, in place (the rule of
 // k_dec_xprep, bit for bit): wave wv of WPB converts rows wv, wv + WPB, ...
@@ -673,17 +670,18 @@ __global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_gate_up_cu(
 // Then the block takes its share of the active units as k_dec_gate_up_cu
 // does, with the group metadata from LDS.  Same arithmetic as the separate
 // launches, so the same bits (with KS > 1, the same bits as k_dec_gate_up's
-// split of the same KS).
-// DP: code chunks in flight per wave (kGuPipe, or kGuPipeFew when blocks hold
-// only a few units and the memory system would otherwise idle).
+// split of the same KS).  (Issuing each wave's first unit loads before the
+// permutation's second half, from the union of the token bitmaps, measured
+// slower: the waves then stall issuing into the full memory pipeline and the
+// permutation ends about 3 us later at T = 8.)
 // KS > 1 (split K, for launches whose blocks hold at most kGuCuWaves / KS
 // units): the block's waves work in rounds of kGuCuWaves / KS units, KS
-// consecutive waves per unit, each on NCH / KS consecutive chunks with the
-// unit's scale runs in its own LDS slot; waves 1 .. KS-1 of a unit leave their
-// partial sums in their slots, and after a barrier the unit's first wave adds
-// them in wave order (a fixed order: the result does not depend on timing)
-// and runs the epilogue.  Every wave takes part in every round's barriers.
-template <int NCH, int TR, bool FP8, int MAXV, int KS, int DP>
+// consecutive waves per unit, each on NCH / KS consecutive chunks (all of
+// them in flight at once) with the unit's scale runs in its own LDS slot;
+// waves 1 .. KS-1 of a unit leave their partial sums in their slots, and
+// after a barrier the unit's first wave adds them in wave order (a fixed
+// order: the result does not depend on timing) and runs the epilogue.  Every wave takes part in every round's barriers.
+template <int NCH, int TR, bool FP8, int MAXV, int KS>
 __global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_layer_gate_up(
     const float* __restrict__ logits, int E, const uint8_t* __restrict__ gu_codes,
     const uint8_t* __restrict__ gu_scales, const float* __restrict__ scale2,
@@ -697,7 +695,7 @@ __global__ __launch_bounds__(64 * kGuCuWaves) void k_dec_layer_gate_up(
   constexpr int CPR = 16 * NCH;                     // 16-byte chunks per row, H = 128 * NCH
   constexpr int SRUN = 128 * NCH;                   // scale bytes of 16 rows
   constexpr int NCK = NCH / KS;                     // chunks per wave
-  constexpr int D = NCK < DP ? NCK : DP;
+  constexpr int D = KS > 1 ? NCK : (NCH < kGuPipe ? NCH : kGuPipe);  // chunks in flight
   constexpr int SLOT = dec_layer_slot_bytes(NCH, KS);
   const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1047,22 +1045,20 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
 // --------------------------------- host -----------------------------------
 
 // The decode layer kernel's variants of one (NCH, TR, MAXV): K split over 1,
-// 2, 4 or 8 waves (where NCH allows), and without the split, the two pipeline
-// depths.
-template <int NCH, int TR, int MV, int KS, int DP>
+// 2, 4 or 8 waves (where NCH allows).
+template <int NCH, int TR, int MV, int KS>
 static void reg_dec_layer_gate_up1(std::vector<const void*>& k) {
   if constexpr (NCH % KS == 0) {
-    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, false, MV, KS, DP>);
-    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, true, MV, KS, DP>);
+    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, false, MV, KS>);
+    k.push_back((const void*)&k_dec_layer_gate_up<NCH, TR, true, MV, KS>);
   }
 }
 template <int NCH, int TR, int MV>
 static void reg_dec_layer_gate_up(std::vector<const void*>& k) {
-  reg_dec_layer_gate_up1<NCH, TR, MV, 1, kGuPipe>(k);
-  reg_dec_layer_gate_up1<NCH, TR, MV, 1, kGuPipeFew>(k);
-  reg_dec_layer_gate_up1<NCH, TR, MV, 2, kGuPipeFew>(k);
-  reg_dec_layer_gate_up1<NCH, TR, MV, 4, kGuPipeFew>(k);
-  reg_dec_layer_gate_up1<NCH, TR, MV, 8, kGuPipeFew>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 1>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 2>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 4>(k);
+  reg_dec_layer_gate_up1<NCH, TR, MV, 8>(k);
 }
 
 void register_decode_kernels(std::vector<const void*>& k) {
@@ -1187,9 +1183,6 @@ static void launch_dec_gate_up(const moe_nvfp4_weights& W, const uint16_t* x, in
 
 // Split K below this many gate_up units per CU (see k_dec_gate_up).
 constexpr long kGuSplitBelow = 2;
-// The decode layer kernel keeps kGuPipeFew chunks in flight per wave below
-// this many gate_up units per CU (a wave then streams its whole unit alone).
-constexpr long kLayerDeepBelow = 4;
 // K split of the decode layer kernel: at most kLayerSplitMaxKs waves per
 // unit, and only while a block holds at most kLayerSplitMaxShare units.
 // Measured at H = 2048, I = 512, E = 512, K = 10 (whole layer, weights cold):
@@ -1331,27 +1324,25 @@ bool decode_layer_supported(int T, int E, int K, int H, int I, int act_mode) {
          (act_mode == MOE_ACT_BF16 || act_mode == MOE_ACT_FP8_ROW);
 }
 
-// The decode layer kernel for one (NCH, TR, FP8, MAXV): the K split `ks` and,
-// without a split, the pipeline depth.
+// The decode layer kernel for one (NCH, TR, FP8, MAXV) and the K split `ks`.
 template <int NCH, int TR, bool F8, int MV>
-static void launch_dec_layer_gu(int ks, bool deep, const moe_nvfp4_weights& W, const float* logits,
+static void launch_dec_layer_gu(int ks, const moe_nvfp4_weights& W, const float* logits,
                                 const uint16_t* x, int T, int K, const RpOut& ro, uint16_t* hbuf,
                                 uint8_t* xq, float* xs, hipStream_t s) {
   const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
   const dim3 grid((unsigned)num_cus()), block(64 * kGuCuWaves);
   const size_t lds = (size_t)TR * H * 2 + 256 + (size_t)kGuCuWaves * dec_layer_slot_bytes(NCH, ks);
-#define MOE_DEC_LGU0(KS, DP)                                                                     \
-  MOE_LAUNCH("dec_gate_up", s, (k_dec_layer_gate_up<NCH, TR, F8, MV, KS, DP>), grid, block, lds, \
+#define MOE_DEC_LGU0(KS)                                                                     \
+  MOE_LAUNCH("dec_gate_up", s, (k_dec_layer_gate_up<NCH, TR, F8, MV, KS>), grid, block, lds, \
              s, logits, E, W.gu_codes, W.gu_scales, W.scale2, x, xq, xs, T, K, H, I, hs, ro, hbuf)
   if constexpr (NCH % 8 == 0) {
-    if (ks == 8) { MOE_DEC_LGU0(8, kGuPipeFew); return; }
+    if (ks == 8) { MOE_DEC_LGU0(8); return; }
   }
   if constexpr (NCH % 4 == 0) {
-    if (ks == 4) { MOE_DEC_LGU0(4, kGuPipeFew); return; }
+    if (ks == 4) { MOE_DEC_LGU0(4); return; }
   }
-  if (ks == 2) MOE_DEC_LGU0(2, kGuPipeFew);
-  else if (deep) MOE_DEC_LGU0(1, kGuPipeFew);
-  else MOE_DEC_LGU0(1, kGuPipe);
+  if (ks == 2) MOE_DEC_LGU0(2);
+  else MOE_DEC_LGU0(1);
 #undef MOE_DEC_LGU0
 }
 
@@ -1375,15 +1366,14 @@ hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, 
   int ks = 1;
   if (share <= kLayerSplitMaxShare)
     while (2 * ks <= kLayerSplitMaxKs && 2 * ks * share <= kGuCuWaves && nch % (2 * ks) == 0) ks *= 2;
-  const bool deep = units < kLayerDeepBelow * num_cus();
 #define MOE_DEC_LGU2(NCH, TR)                                                                     \
   do {                                                                                            \
     if (E <= 512) {                                                                               \
-      if (fp8) launch_dec_layer_gu<NCH, TR, true, 8>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);   \
-      else launch_dec_layer_gu<NCH, TR, false, 8>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);      \
+      if (fp8) launch_dec_layer_gu<NCH, TR, true, 8>(ks, W, logits, x, T, K, ro, hbuf, xq, xs, s);   \
+      else launch_dec_layer_gu<NCH, TR, false, 8>(ks, W, logits, x, T, K, ro, hbuf, xq, xs, s);      \
     } else {                                                                                      \
-      if (fp8) launch_dec_layer_gu<NCH, TR, true, 16>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);  \
-      else launch_dec_layer_gu<NCH, TR, false, 16>(ks, deep, W, logits, x, T, K, ro, hbuf, xq, xs, s);     \
+      if (fp8) launch_dec_layer_gu<NCH, TR, true, 16>(ks, W, logits, x, T, K, ro, hbuf, xq, xs, s);  \
+      else launch_dec_layer_gu<NCH, TR, false, 16>(ks, W, logits, x, T, K, ro, hbuf, xq, xs, s);     \
     }                                                                                             \
   } while (0)
 #define MOE_DEC_LGU(NCH)                    \

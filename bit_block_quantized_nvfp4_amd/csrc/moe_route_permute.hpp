@@ -3,18 +3,21 @@
 // decode layer kernel, whose every block needs the routing of the batch).
 //
 //  * rp_route: every thread clears the group counts (the shared group holds
-//    T); wave t < T routes token t (the router stage's rule, moe_topk.hpp)
-//    into LDS, and into the global ids / w when `write`.  No barrier, so a
-//    caller can give its other waves other work before rp_permute.
-//  * rp_permute (every thread of the block): LDS atomics count the slots;
-//    one exclusive scan of count | (count > 0) << 16 gives both the group
-//    offsets (low 16 bits; at most kRouteFuseMaxT * 33 slots) and each
-//    non-empty group's index in the compact list (high bits); the rank of
+//    T) and the per-token expert bitmaps; wave t < T routes token t (the
+//    router stage's rule, moe_topk.hpp) into LDS, and into the global ids / w
+//    when `write`.  No barrier, so a caller can give its other waves other
+//    work before rp_permute.
+//  * rp_permute (every thread of the block): LDS atomics count the slots and
+//    mark each slot's expert in its token's bitmap; one exclusive scan of
+//    count | (count > 0) << 16, read straight from the counts, gives both the
+//    group offsets (low 16 bits; at most kRouteFuseMaxT * 33 slots) and each
+//    non-empty group's index in the compact list (high bits).  The rank of
 //    slot s inside its group is the number of earlier slots with the same
-//    expert, counted from the ids in LDS (the stable counting sort of the
-//    multi-block path, without its per-chunk masks).  Leaves in LDS: cnt
-//    (counts), run (offset | list index << 16), gl (the list), ss_l (the
-//    sorted slots); with `write`, the permutation's global outputs too.
+//    expert (the stable counting sort of the multi-block path); the K experts
+//    of one token are distinct, so that is the number of earlier tokens whose
+//    bitmap holds the expert.  Leaves in LDS: cnt (counts), run (offset |
+//    list index << 16), gl (the list), ss_l (the sorted slots); with `write`,
+//    the permutation's global outputs too.
 #pragma once
 
 #include "moe_device.hpp"
@@ -54,11 +57,14 @@ __device__ int block_exclusive_scan(int* a, int n, int* wsum) {
   return total;
 }
 
+constexpr int kRpMapWords = kRpMaxE / 32;         // bitmap words per token
+
 struct RpLds {
   int cnt[kRpMaxE + 1];
   int run[kRpMaxE + 1];
   int gl[kRpMaxE + 1];
   int wsum[16];
+  uint32_t bm[kRouteFuseMaxT][kRpMapWords];       // experts chosen by each token
   __align__(16) int32_t ids_l[kRpMaxSlots];
   float w_l[kRpMaxSlots];
   int32_t ss_l[kRpMaxSlots + kRouteFuseMaxT];
@@ -71,6 +77,7 @@ __device__ __forceinline__ void rp_route(const float* __restrict__ logits, int T
   const int tid = threadIdx.x, wv = tid >> 6;
   const int G = E + has_shared;
   for (int e = tid; e < G; e += NT) L.cnt[e] = (e == E) ? T : 0;
+  for (int i = tid; i < kRouteFuseMaxT * kRpMapWords; i += NT) (&L.bm[0][0])[i] = 0u;
   if (wv < T) {  // uniform per wave
     if (write)
       route_row_topk<MAXV>(logits + (size_t)wv * E, E, K, o.ids + (size_t)wv * K,
@@ -83,47 +90,75 @@ __device__ __forceinline__ void rp_route(const float* __restrict__ logits, int T
 template <int NT>
 __device__ __forceinline__ int rp_permute(int T, int E, int K, int has_shared, bool write,
                                           const RpOut& o, RpLds& L) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = E + has_shared, TK = T * K;
-  __syncthreads();
+  __syncthreads();  // the routed ids, the cleared counts and bitmaps
   const int e_s = tid < TK ? L.ids_l[tid] : -1;
   const bool ok = e_s >= 0 && e_s < E;
-  if (ok) atomicAdd(&L.cnt[e_s], 1);
-  __syncthreads();
-  for (int e = tid; e < G; e += NT) {
-    const int c = L.cnt[e];
-    if (write) o.counts[e] = c;
-    L.run[e] = c | ((c > 0 ? 1 : 0) << 16);
+  const int t_s = tid < TK ? tid / K : 0;
+  if (ok) {
+    atomicAdd(&L.cnt[e_s], 1);
+    atomicOr(&L.bm[t_s][e_s >> 5], 1u << (e_s & 31));
   }
   __syncthreads();
-  const int packed = block_exclusive_scan<NT>(L.run, G, L.wsum);
-  const int nz = packed >> 16;
-  for (int e = tid; e < G; e += NT) {
-    const int v = L.run[e];
-    if (write) o.offsets[e] = v & 0xFFFF;
-    if (L.cnt[e] > 0) {
-      L.gl[v >> 16] = e;
-      if (write) o.groups[1 + (v >> 16)] = e;
+  // rank of slot tid in its group: the earlier tokens that chose its expert
+  int rank = 0;
+  if (ok) {
+#pragma unroll
+    for (int u = 0; u + 1 < kRouteFuseMaxT; ++u)
+      if (u < t_s) rank += (int)((L.bm[u][e_s >> 5] >> (e_s & 31)) & 1u);
+  }
+  // exclusive scan of count | (count > 0) << 16 over the G groups, PER
+  // consecutive groups per thread
+  constexpr int PER = (kRpMaxE + 1 + NT - 1) / NT;
+  const int lo = tid * PER;
+  int v[PER];
+  int local = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c = lo + p < G ? L.cnt[lo + p] : 0;
+    v[p] = c | ((c > 0 ? 1 : 0) << 16);
+    local += v[p];
+  }
+  const int incl = wave_incl_scan(local, lane);
+  if (lane == 63) L.wsum[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    before += (i < wv) ? L.wsum[i] : 0;
+    total += L.wsum[i];
+  }
+  int run = before + incl - local;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int e = lo + p;
+    if (e < G) {
+      const int c = v[p] & 0xFFFF;
+      L.run[e] = run;
+      if (write) {
+        o.counts[e] = c;
+        o.offsets[e] = run & 0xFFFF;
+      }
+      if (c > 0) {
+        L.gl[run >> 16] = e;
+        if (write) o.groups[1 + (run >> 16)] = e;
+      }
     }
+    run += v[p];
   }
+  const int nz = total >> 16;
   if (write) {
     for (int i = nz + tid; i < G; i += NT) o.groups[1 + i] = -1;  // deterministic tail
     if (tid == 0) {
-      o.offsets[G] = packed & 0xFFFF;
+      o.offsets[G] = total & 0xFFFF;
       o.groups[0] = nz;
     }
   }
+  __syncthreads();
   if (tid < TK) {
-    int pos = -1;
+    const int pos = ok ? (L.run[e_s] & 0xFFFF) + rank : -1;
     if (ok) {
-      int r = 0;
-      const int s4 = tid & ~3;
-      for (int j = 0; j < s4; j += 4) {
-        const int4 v = *(const int4*)(L.ids_l + j);
-        r += (v.x == e_s) + (v.y == e_s) + (v.z == e_s) + (v.w == e_s);
-      }
-      for (int j = s4; j < tid; ++j) r += L.ids_l[j] == e_s;
-      pos = (L.run[e_s] & 0xFFFF) + r;
       L.ss_l[pos] = tid;
       if (write) o.sorted_slot[pos] = tid;
     }

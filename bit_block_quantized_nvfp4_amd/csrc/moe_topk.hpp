@@ -59,14 +59,27 @@ __device__ __forceinline__ void route_rows_topk(const float* const (&rows)[R], c
                                                 int32_t* const (&ids_copy)[R]) {
   const int lane = threadIdx.x & 63;
   uint32_t key[R][MAXV], jx[R][MAXV];  // key and slot j (expert lane + 64 j) of each entry
+  // every load of a row is issued before the first is consumed: the index is
+  // clamped into the row (E >= 1) instead of guarding each load, which would
+  // make each one a separate round trip to memory
+  float zr[R][MAXV];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (live[r]) {  // uniform per wave
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) zr[r][j] = rows[r][min(lane + 64 * j, E - 1)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < MAXV; ++j) zr[r][j] = -INFINITY;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
       const int e = lane + 64 * j;
       const bool in = live[r] && e < E;
-      float z = -INFINITY;
-      if (in) z = rows[r][e];
+      const float z = zr[r][j];
       // absent elements get key 0, below every real key (-inf maps to 0x007FFFFF)
       key[r][j] = in ? logit_key((z != z) ? -INFINITY : z) : 0u;
       jx[r][j] = (uint32_t)j;
