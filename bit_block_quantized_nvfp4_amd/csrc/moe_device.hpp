@@ -52,13 +52,21 @@ __device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
 // (quad permutes), half-row and row mirrors leave each row's max in all its
 // lanes; row broadcasts of lane 15 (into rows 1, 3) and lane 31 (into rows
 // 2, 3) leave the wave's max in lane 63.
+// Each step moves with 0 (the identity of the max) in the lanes a row mask
+// leaves out, which lets the compiler fold the move into the max (one DPP
+// max per step).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp<0xB1>(v));
-  v = max(v, dpp<0x4E>(v));
-  v = max(v, dpp<0x141>(v));
-  v = max(v, dpp<0x140>(v));
-  v = max(v, dpp_rows<0x142, 0xA>(v));
-  v = max(v, dpp_rows<0x143, 0xC>(v));
+  auto mv = [](uint32_t x, auto ctrl, auto rows) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value,
+                                                 decltype(rows)::value, 0xF, false);
+  };
+  using RA = std::integral_constant<int, 0xF>;
+  v = max(v, mv(v, std::integral_constant<int, 0xB1>{}, RA{}));
+  v = max(v, mv(v, std::integral_constant<int, 0x4E>{}, RA{}));
+  v = max(v, mv(v, std::integral_constant<int, 0x141>{}, RA{}));
+  v = max(v, mv(v, std::integral_constant<int, 0x140>{}, RA{}));
+  v = max(v, mv(v, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{}));
+  v = max(v, mv(v, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{}));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // Sum over the 64 lanes, as a uniform value, in a fixed order and without

@@ -7,17 +7,19 @@
 //    router stage's rule, moe_topk.hpp) into LDS, and into the global ids / w
 //    when `write`.  No barrier, so a caller can give its other waves other
 //    work before rp_permute.
-//  * rp_permute (every thread of the block): LDS atomics count the slots and
-//    mark each slot's expert in its token's bitmap; one exclusive scan of
-//    count | (count > 0) << 16, read straight from the counts, gives both the
-//    group offsets (low 16 bits; at most kRouteFuseMaxT * 33 slots) and each
-//    non-empty group's index in the compact list (high bits).  The rank of
-//    slot s inside its group is the number of earlier slots with the same
-//    expert (the stable counting sort of the multi-block path); the K experts
-//    of one token are distinct, so that is the number of earlier tokens whose
-//    bitmap holds the expert.  Leaves in LDS: cnt (counts), run (offset |
-//    list index << 16), gl (the list), ss_l (the sorted slots); with `write`,
-//    the permutation's global outputs too.
+//  * rp_permute (every thread of the block) places the routed slots in the
+//    stable counting-sort order of the multi-block path without a scan over
+//    the groups: LDS atomics count the slots per expert and mark each slot's
+//    expert in its token's bitmap; one wave then takes, per 32-expert word,
+//    the number of slots (the tokens' bitmap populations) and of distinct
+//    experts (the union's population), and their exclusive prefixes over the
+//    words.  A slot with expert e then finds the slots of smaller experts
+//    (the word prefix plus the tokens' bits below e in e's word), its rank
+//    among the slots of e (the earlier tokens whose bitmap holds e: the K
+//    experts of a token are distinct) and e's index in the compact list (the
+//    same from the union).  Leaves in LDS: cnt (counts), run (offset | list
+//    index << 16) and gl (the list) for the active groups, ss_l (the sorted
+//    slots); with `write`, the permutation's global outputs for every group.
 #pragma once
 
 #include "moe_device.hpp"
@@ -63,8 +65,10 @@ struct RpLds {
   int cnt[kRpMaxE + 1];
   int run[kRpMaxE + 1];
   int gl[kRpMaxE + 1];
-  int wsum[16];
   uint32_t bm[kRouteFuseMaxT][kRpMapWords];       // experts chosen by each token
+  uint32_t un[kRpMapWords];                       // their union
+  int pre_s[kRpMapWords + 1];                     // slots of experts in words < w
+  int pre_g[kRpMapWords + 1];                     // distinct experts in words < w
   __align__(16) int32_t ids_l[kRpMaxSlots];
   float w_l[kRpMaxSlots];
   int32_t ss_l[kRpMaxSlots + kRouteFuseMaxT];
@@ -101,6 +105,26 @@ __device__ __forceinline__ int rp_permute(int T, int E, int K, int has_shared, b
     atomicOr(&L.bm[t_s][e_s >> 5], 1u << (e_s & 31));
   }
   __syncthreads();
+  if (wv == 0) {  // per word: slots and distinct experts, exclusive prefixes
+    uint32_t u = 0u;
+    int ns = 0;
+    if (lane < kRpMapWords) {
+#pragma unroll
+      for (int t = 0; t < kRouteFuseMaxT; ++t)
+        if (t < T) {
+          const uint32_t m = L.bm[t][lane];
+          u |= m;
+          ns += __popc(m);
+        }
+      L.un[lane] = u;
+    }
+    const int ng = __popc(u);
+    const int is = wave_incl_scan(ns, lane), ig = wave_incl_scan(ng, lane);
+    if (lane <= kRpMapWords) {  // lane 32 holds the totals
+      L.pre_s[lane] = is - ns;
+      L.pre_g[lane] = ig - ng;
+    }
+  }
   // rank of slot tid in its group: the earlier tokens that chose its expert
   int rank = 0;
   if (ok) {
@@ -108,70 +132,59 @@ __device__ __forceinline__ int rp_permute(int T, int E, int K, int has_shared, b
     for (int u = 0; u + 1 < kRouteFuseMaxT; ++u)
       if (u < t_s) rank += (int)((L.bm[u][e_s >> 5] >> (e_s & 31)) & 1u);
   }
-  // exclusive scan of count | (count > 0) << 16 over the G groups, PER
-  // consecutive groups per thread
-  constexpr int PER = (kRpMaxE + 1 + NT - 1) / NT;
-  const int lo = tid * PER;
-  int v[PER];
-  int local = 0;
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int c = lo + p < G ? L.cnt[lo + p] : 0;
-    v[p] = c | ((c > 0 ? 1 : 0) << 16);
-    local += v[p];
-  }
-  const int incl = wave_incl_scan(local, lane);
-  if (lane == 63) L.wsum[wv] = incl;
   __syncthreads();
-  int before = 0, total = 0;
+  // slots of experts below e (e < E)
+  auto slots_below = [&](int e) {
+    const int w = e >> 5;
+    const uint32_t below = (1u << (e & 31)) - 1u;
+    int c = L.pre_s[w];
 #pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    before += (i < wv) ? L.wsum[i] : 0;
-    total += L.wsum[i];
-  }
-  int run = before + incl - local;
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int e = lo + p;
-    if (e < G) {
-      const int c = v[p] & 0xFFFF;
-      L.run[e] = run;
-      if (write) {
-        o.counts[e] = c;
-        o.offsets[e] = run & 0xFFFF;
-      }
-      if (c > 0) {
-        L.gl[run >> 16] = e;
-        if (write) o.groups[1 + (run >> 16)] = e;
-      }
-    }
-    run += v[p];
-  }
-  const int nz = total >> 16;
-  if (write) {
-    for (int i = nz + tid; i < G; i += NT) o.groups[1 + i] = -1;  // deterministic tail
-    if (tid == 0) {
-      o.offsets[G] = total & 0xFFFF;
-      o.groups[0] = nz;
-    }
-  }
-  __syncthreads();
+    for (int t = 0; t < kRouteFuseMaxT; ++t)
+      if (t < T) c += __popc(L.bm[t][w] & below);
+    return c;
+  };
+  const int nzr = L.pre_g[kRpMapWords], tkv = L.pre_s[kRpMapWords];
+  const int nz = nzr + has_shared;
   if (tid < TK) {
-    const int pos = ok ? (L.run[e_s] & 0xFFFF) + rank : -1;
+    int pos = -1;
     if (ok) {
+      const int off = slots_below(e_s);
+      pos = off + rank;
       L.ss_l[pos] = tid;
       if (write) o.sorted_slot[pos] = tid;
+      if (rank == 0) {  // the group's first slot publishes the group
+        const int w = e_s >> 5;
+        const int li = L.pre_g[w] + __popc(L.un[w] & ((1u << (e_s & 31)) - 1u));
+        L.gl[li] = e_s;
+        L.run[e_s] = off | (li << 16);
+        if (write) o.groups[1 + li] = e_s;
+      }
     }
     if (write) o.slot_pos[tid] = pos;
   }
-  if (has_shared) {  // slot T*K + t sits at position off + t, both ways
-    const int off = L.run[E] & 0xFFFF;
+  if (has_shared) {  // the shared group is the last one; slot T*K + t at tkv + t
+    if (tid == 0) {
+      L.gl[nzr] = E;
+      L.run[E] = tkv | (nzr << 16);
+      if (write) o.groups[1 + nzr] = E;
+    }
     for (int t = tid; t < T; t += NT) {
-      L.ss_l[off + t] = TK + t;
+      L.ss_l[tkv + t] = TK + t;
       if (write) {
-        o.sorted_slot[off + t] = TK + t;
-        o.slot_pos[TK + t] = off + t;
+        o.sorted_slot[tkv + t] = TK + t;
+        o.slot_pos[TK + t] = tkv + t;
       }
+    }
+  }
+  if (write) {  // counts and offsets of every group, the list's tail
+    for (int e = tid; e < G; e += NT) {
+      o.counts[e] = L.cnt[e];
+      o.offsets[e] = e < E ? slots_below(e) : tkv;
+    }
+    for (int i = nz + tid; i < G; i += NT) o.groups[1 + i] = -1;  // deterministic tail
+    if (tid == 0) {
+      o.offsets[G] = tkv + (has_shared ? T : 0);
+      o.groups[0] = nz;
     }
   }
   __syncthreads();
