@@ -3,8 +3,10 @@
 // g_t = 1, or sigmoid(gate[t]) for a gated shared expert; fp32 accumulation in
 // slot order, then the shared expert, one rounding at the end (the same-order
 // rule for per-slot expert outputs of the issue "EXL3 Qwen3.8-Flash-Next on
-// CUDA sm_120 ...", expert-parallel TP=2).  Used by the combine kernel and by
-// the down kernel's combine tail, so both give the same bits.
+// CUDA sm_120 ...", expert-parallel TP=2).  combine_rows reads the 8 values
+// of slot position p at yrow(p): the combine kernel reads y in global memory,
+// the decode down + combine kernel its LDS copy of the same values, so both
+// give the same bits.
 #pragma once
 
 #include <math.h>
@@ -13,12 +15,11 @@
 
 namespace moe {
 
-__device__ __forceinline__ void combine_chunk(const uint16_t* __restrict__ y,
-                                              const float* __restrict__ w,
-                                              const int32_t* __restrict__ slot_pos,
-                                              const float* __restrict__ gate, int T, int K, int H,
-                                              int has_shared, uint16_t* __restrict__ out, int t,
-                                              int col) {
+template <typename YRow>
+__device__ __forceinline__ void combine_rows(YRow yrow, const float* __restrict__ w,
+                                             const int32_t* __restrict__ slot_pos,
+                                             const float* __restrict__ gate, int T, int K,
+                                             int has_shared, uint16_t* __restrict__ dst, int t) {
   const int TK = T * K;
   float acc[8];
 #pragma unroll
@@ -38,8 +39,7 @@ __device__ __forceinline__ void combine_chunk(const uint16_t* __restrict__ y,
     u32x4 v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      v[j] = (p[j] >= 0 && p[j] < TK) ? *(const u32x4*)(y + (size_t)p[j] * H + col)
-                                      : u32x4{0u, 0u, 0u, 0u};
+      v[j] = (p[j] >= 0 && p[j] < TK) ? *(const u32x4*)yrow(p[j]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (p[j] >= 0 && p[j] < TK) {
@@ -52,7 +52,7 @@ __device__ __forceinline__ void combine_chunk(const uint16_t* __restrict__ y,
     }
   }
   if (ps >= 0 && ps < TK + T) {
-    const u32x4 v = *(const u32x4*)(y + (size_t)ps * H + col);
+    const u32x4 v = *(const u32x4*)yrow(ps);
     if (gate) {  // sigmoid-gated shared expert
       const float sg = 1.0f / (1.0f + expf(-gate[t]));
 #pragma unroll
@@ -71,7 +71,18 @@ __device__ __forceinline__ void combine_chunk(const uint16_t* __restrict__ y,
   u32x4 o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-  *(u32x4*)(out + (size_t)t * H + col) = o;
+  *(u32x4*)dst = o;
+}
+
+// Columns [col, col + 8) of token t, with y [S][H] in global memory.
+__device__ __forceinline__ void combine_chunk(const uint16_t* __restrict__ y,
+                                              const float* __restrict__ w,
+                                              const int32_t* __restrict__ slot_pos,
+                                              const float* __restrict__ gate, int T, int K, int H,
+                                              int has_shared, uint16_t* __restrict__ out, int t,
+                                              int col) {
+  combine_rows([&](int p) { return y + (size_t)p * H + col; }, w, slot_pos, gate, T, K, has_shared,
+               out + (size_t)t * H + col, t);
 }
 
 }  // namespace moe

@@ -133,9 +133,8 @@ hipError_t launch_layer(const moe_nvfp4_weights& W, const float* logits, const u
       wp += align256((size_t)T * H);
       xs = (float*)wp;
     }
-    hipError_t e = launch_decode_layer(W, logits, x, T, K, act_mode, ro, hbuf, xq, xs, y_slots, s);
-    if (e != hipSuccess) return e;
-    return launch_combine(y_slots, ro.w, ro.slot_pos, gate, T, K, H, hs, out, s);
+    return launch_decode_layer(W, logits, x, T, K, act_mode, gate, ro, hbuf, xq, xs, y_slots, out,
+                               s);
   }
   hipError_t e = launch_route_permute(logits, T, E, K, hs, ro.ids, ro.w, ro.counts, ro.offsets,
                                       ro.sorted_slot, ro.slot_pos, ro.groups, ws, s);

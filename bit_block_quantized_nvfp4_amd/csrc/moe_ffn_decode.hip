@@ -41,6 +41,7 @@
 // element 128c + 32q + 8j + i on both operands, so the sum is over all of K.
 #include <type_traits>
 
+#include "moe_combine.hpp"
 #include "moe_ffn_common.hpp"
 #include "moe_internal.hpp"
 #include "moe_route_permute.hpp"
@@ -1042,6 +1043,136 @@ __global__ __launch_bounds__(64 * WPB) void k_dec_down(
   }
 }
 
+// ------------------------- down + combine (small T) ------------------------
+// The decode layer's down and combine in one launch, for batches routed by
+// the layer itself: the K experts of a token are distinct, so a group holds
+// at most T positions (TR = T rounded up to 1, 2, 4 or 8 rows).  Block b takes
+// the output columns [16 b, 16 b + 16) of every active group; wave w takes
+// groups w, w + kDcWaves, ... and computes each exactly as a 16-row
+// k_dec_down unit does (the group's h rows staged and converted with the same
+// per-row power of two, in this wave's own LDS region; the same MFMA order
+// and epilogue), so y has the same bits; it writes y and keeps a copy of its
+// rows in LDS.  After one barrier the block combines its 16 columns of every
+// token from that copy (combine_rows: the combine kernel's arithmetic, the
+// same bits).  No block waits for another.
+// Dynamic LDS: per wave [TR][I] h rows; per wave 16 row factors (f32); per
+// wave the unit's scale run (16 x I/16 B); then the y copy [S][16] (bf16).
+constexpr int kDcWaves = 16;
+
+template <int NCH, int TR>   // NCH = I / 128
+__global__ __launch_bounds__(64 * kDcWaves) void k_dec_down_combine(
+    const uint8_t* __restrict__ dn_codes, const uint8_t* __restrict__ dn_scales,
+    const float* __restrict__ scale2, const uint16_t* __restrict__ h,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ groups,
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos,
+    const float* __restrict__ gate, int T, int K, int H, int I, int has_shared,
+    uint16_t* __restrict__ y, uint16_t* __restrict__ out) {
+  constexpr int WPB = kDcWaves;
+  constexpr int CPR = 16 * NCH;       // 16-byte chunks of an h row
+  constexpr int SRUN = 128 * NCH;     // scale bytes of 16 rows
+  constexpr int HW = TR * CPR * 16;   // bytes of a wave's h rows
+  constexpr int NCLD = (CPR + 63) / 64;
+  extern __shared__ __align__(16) uint8_t dl[];
+  const int lane = threadIdx.x & 63, r16 = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* hw = dl + (size_t)wv * HW;
+  float* hfac = (float*)(dl + (size_t)WPB * HW) + 16 * wv;
+  uint8_t* sl = dl + (size_t)WPB * HW + WPB * 64 + (size_t)wv * SRUN;
+  uint16_t* yl = (uint16_t*)(dl + (size_t)WPB * (HW + 64 + SRUN));
+  const int col0 = blockIdx.x * 16;
+  const int nact = groups[0];
+  const size_t rowb = (size_t)I / 2;
+  // A operand of sub-MFMA (c, j) at haoff[j] + 256 c; MFMA rows past TR read
+  // row TR - 1 (their outputs are never stored)
+  const int xr = r16 < TR ? r16 : TR - 1;
+  int haoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) haoff[j] = swz_off(xr, 4 * q + j, CPR);
+  const uint8_t* srow = sl + r16 * (8 * NCH) + 2 * q;
+  for (int a = wv; a < nact; a += WPB) {  // uniform per wave
+    const int e = __builtin_amdgcn_readfirstlane(groups[1 + a]);
+    const int p0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+    // n <= T <= TR by the routing; the clamp only keeps LDS in bounds
+    const int nn = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - p0;
+    const int n = nn < TR ? nn : TR;
+    const size_t row0 = (size_t)e * H + col0;
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): the last group's LDS reads
+    // scale run, the group's h rows, then every code chunk
+    dma_run<SRUN>(dn_scales + row0 * (I / 16), sl, lane);
+    dma_rows_swizzled(hw, n, CPR, 0, 1, lane,
+                      [&](int r) { return (const uint8_t*)(h + (size_t)(p0 + r) * I); });
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 wc[NCH];
+    const uint8_t* cr = dn_codes + (row0 + r16) * rowb + 16 * q;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) wc[c] = *(const u32x4*)(cr + 64 * c);
+    __builtin_amdgcn_sched_barrier(0);
+    const float s2d = scale2[3 * e + 2];
+    wait_vmcnt<NCH>();  // the scale run and the h rows have landed
+    // the h rows -> f16 in place, each times the power of two that brings its
+    // absmax into [2^14, 2^15), undone in the epilogue (k_dec_down's rule)
+    for (int r = 0; r < n; ++r) {
+      u32x4 v[NCLD];
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k) {
+        const int ch = lane + 64 * k;
+        v[k] = ch < CPR ? *(const u32x4*)(hw + swz_off(r, ch, CPR)) : u32x4{0u, 0u, 0u, 0u};
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][jj] & 0xFFFFu)));
+          amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[k][jj] >> 16)));
+        }
+      amax = wave_max_nonneg(amax);  // fmaxf drops NaN: every lane is >= 0, not NaN
+      const int sh = f16_row_shift(amax);
+      const float mul = ldexpf(1.0f, sh);
+      if (lane == 0) hfac[r] = ldexpf(1.0f, -sh);
+#pragma unroll
+      for (int k = 0; k < NCLD; ++k) {
+        const int ch = lane + 64 * k;
+        if (ch >= CPR) break;
+        u32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          o[jj] = pack_f16x2(bf16_bits_to_f32(v[k][jj] & 0xFFFFu) * mul,
+                             bf16_bits_to_f32(v[k][jj] >> 16) * mul);
+        *(u32x4*)(hw + swz_off(r, ch, CPR)) = o;
+      }
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    static_for<0, NCH>([&](auto ct) {
+      constexpr int c = decltype(ct)::value;
+      wait_vmcnt<NCH - c - 1>();
+      const f16x2 sc = e4m3x2_to_f16(*(const uint16_t*)(srow + 8 * c));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 av = __builtin_bit_cast(f16x8, *(const u32x4*)(hw + haoff[j] + 256 * c));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dqh8(wc[c][j], j < 2 ? sc.x : sc.y), acc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mm = 4 * q + i;
+      if (mm < n) {
+        const uint16_t v = f32_to_bf16_bits(acc[i] * hfac[mm] * s2d);
+        y[(size_t)(p0 + mm) * H + col0 + r16] = v;
+        yl[(size_t)(p0 + mm) * 16 + r16] = v;
+      }
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < 2 * T) {  // token t, columns col0 + 8 half .. + 8
+    const int t = threadIdx.x >> 1, half = threadIdx.x & 1;
+    combine_rows([&](int pp) { return yl + (size_t)pp * 16 + 8 * half; }, w, slot_pos, gate, T, K,
+                 has_shared, out + (size_t)t * H + col0 + 8 * half, t);
+  }
+}
+
 // --------------------------------- host -----------------------------------
 
 // The decode layer kernel's variants of one (NCH, TR, MAXV): K split over 1,
@@ -1123,6 +1254,15 @@ void register_decode_kernels(std::vector<const void*>& k) {
   MOE_REG_DN(4)
   MOE_REG_DN(8)
 #undef MOE_REG_DN
+#define MOE_REG_DC(NCH)                                        \
+  k.push_back((const void*)&k_dec_down_combine<NCH, 1>); \
+  k.push_back((const void*)&k_dec_down_combine<NCH, 2>); \
+  k.push_back((const void*)&k_dec_down_combine<NCH, 4>); \
+  k.push_back((const void*)&k_dec_down_combine<NCH, 8>);
+  MOE_REG_DC(2)
+  MOE_REG_DC(4)
+  MOE_REG_DC(8)
+#undef MOE_REG_DC
 }
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1346,15 +1486,67 @@ static void launch_dec_layer_gu(int ks, const moe_nvfp4_weights& W, const float*
 #undef MOE_DEC_LGU0
 }
 
+// Down + combine of the decode layer in one launch (k_dec_down_combine) up
+// to this many active groups; above it the down kernel's more, shorter units
+// and the combine kernel.  Measured at H = 2048, I = 512, E = 512, K = 10
+// (whole layer, weights cold), fused / separate: T = 1 16.7 / 18.7 us, T = 2
+// 21.3 / 22.3, T = 4 29.6 / 29.7, T = 6 36.6 / 36.6, T = 8 44.3 / 41.9 (the
+// fused launch has H / 16 blocks, too few once every group is long).
+constexpr int kDcMaxGroups = 48;
+
+// Whether k_dec_down_combine takes this launch: I / 128 in {2, 4, 8}, H a
+// multiple of 16, the LDS of TR h rows per wave within the CU's.
+static size_t dec_down_combine_lds(int T, int K, int I, int hs) {
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
+  const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
+  return (size_t)kDcWaves * ((size_t)tr * I * 2 + 64 + (size_t)I) + S * 32;
+}
+static bool dec_down_combine_ok(int T, int K, int H, int I, int hs, int gmax) {
+  const int ncd = I / 128;
+  return (ncd == 2 || ncd == 4 || ncd == 8) && H % 16 == 0 && gmax <= kDcMaxGroups &&
+         dec_down_combine_lds(T, K, I, hs) <= (size_t)160 * 1024;
+}
+
+static hipError_t launch_dec_down_combine(const moe_nvfp4_weights& W, int T, int K,
+                                          const float* gate, const RpOut& ro,
+                                          const uint16_t* hbuf, uint16_t* y, uint16_t* out,
+                                          hipStream_t s) {
+  const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
+  const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
+  const size_t lds = dec_down_combine_lds(T, K, I, hs);
+  const dim3 grid((unsigned)(H / 16)), block(64 * kDcWaves);
+  const int ncd = I / 128;
+#define MOE_DEC_DC0(NCH, TR)                                                                       \
+  MOE_LAUNCH("dec_down", s, (k_dec_down_combine<NCH, TR>), grid, block, lds, s, W.dn_codes,       \
+             W.dn_scales, W.scale2, hbuf, ro.offsets, ro.groups, ro.w, ro.slot_pos, gate, T, K, H, \
+             I, hs, y, out)
+#define MOE_DEC_DC(NCH)                    \
+  do {                                     \
+    if (tr == 1) MOE_DEC_DC0(NCH, 1);      \
+    else if (tr == 2) MOE_DEC_DC0(NCH, 2); \
+    else if (tr == 4) MOE_DEC_DC0(NCH, 4); \
+    else MOE_DEC_DC0(NCH, 8);              \
+  } while (0)
+  if (ncd == 2) MOE_DEC_DC(2);
+  else if (ncd == 4) MOE_DEC_DC(4);
+  else if (ncd == 8) MOE_DEC_DC(8);
+  else return hipErrorInvalidValue;
+#undef MOE_DEC_DC
+#undef MOE_DEC_DC0
+  return hipGetLastError();
+}
+
 // One block per CU: routing + permutation + gate_up (k_dec_layer_gate_up),
-// then the down launch.  When a block's share of units is at most
+// then down and combine (k_dec_down_combine, or the down and combine
+// kernels).  When a block's share of units is at most
 // kLayerSplitMaxShare, the K split is the largest of 8, 4, 2 (dividing
 // H / 128, at most kLayerSplitMaxKs) whose waves cover every unit of the
 // share in one round; the share is bounded with the most groups the batch
 // can activate, min(T K, E) (+ the shared expert).
 hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x,
-                               int T, int K, int act_mode, const RpOut& ro, uint16_t* hbuf,
-                               uint8_t* xq, float* xs, uint16_t* y, hipStream_t s) {
+                               int T, int K, int act_mode, const float* gate, const RpOut& ro,
+                               uint16_t* hbuf, uint8_t* xq, float* xs, uint16_t* y,
+                               uint16_t* out, hipStream_t s) {
   const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
   const int G = E + hs;
   const int gmax = (int)((long)T * K + hs < (long)G ? (long)T * K + hs : (long)G);
@@ -1390,7 +1582,13 @@ hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, 
   else return hipErrorInvalidValue;
 #undef MOE_DEC_LGU
 #undef MOE_DEC_LGU2
-  return launch_dec_down_all(W, gmax, ro.offsets, ro.groups, hbuf, y, s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (dec_down_combine_ok(T, K, H, I, hs, gmax))
+    return launch_dec_down_combine(W, T, K, gate, ro, hbuf, y, out, s);
+  err = launch_dec_down_all(W, gmax, ro.offsets, ro.groups, hbuf, y, s);
+  if (err != hipSuccess) return err;
+  return launch_combine(y, ro.w, ro.slot_pos, gate, T, K, H, hs, out, s);
 }
 
 }  // namespace moe

@@ -106,12 +106,13 @@ struct RpOut {
   int32_t* groups;
 };
 // The decode layer kernels (routing and permutation inside the gate_up
-// launch, then down): batches of up to kRouteFuseMaxT tokens, the bf16 and
-// the FP8 row arms, decode-supported H and I.
+// launch, then down and combine): batches of up to kRouteFuseMaxT tokens, the
+// bf16 and the FP8 row arms, decode-supported H and I.
 bool decode_layer_supported(int T, int E, int K, int H, int I, int act_mode);
 hipError_t launch_decode_layer(const moe_nvfp4_weights& W, const float* logits, const uint16_t* x,
-                               int T, int K, int act_mode, const RpOut& ro, uint16_t* hbuf,
-                               uint8_t* xq, float* xs, uint16_t* y, hipStream_t s);
+                               int T, int K, int act_mode, const float* gate, const RpOut& ro,
+                               uint16_t* hbuf, uint8_t* xq, float* xs, uint16_t* y,
+                               uint16_t* out, hipStream_t s);
 // The whole layer (moe_layer): the decode layer kernels and the combine, or
 // route+permute and the expert FFN + combine.
 size_t layer_workspace_bytes(int T, int E, int K, int H, int I, int has_shared, int act_mode);

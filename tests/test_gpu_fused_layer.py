@@ -201,6 +201,13 @@ def _layer_vs_calls(moe, wl, act_mode=0, gate=None):
         assert torch.equal(again[nm], ref), nm
     assert torch.equal(one["y_slots"].view(torch.int16), again["y_slots"].view(torch.int16))
     assert torch.equal(one["out"].view(torch.int16), again["out"].view(torch.int16))
+    # the layer's combine (inside the down launch for small batches) is the
+    # combine kernel's arithmetic on the layer's own y rows, bit for bit
+    out_c = (moe.moe_combine(one["y_slots"], one["w"], one["slot_pos"], wl.K, wl.has_shared)
+             if gate is None else
+             moe.moe_combine_gated(one["y_slots"], one["w"], one["slot_pos"], gate, wl.K))
+    torch.cuda.synchronize()
+    assert torch.equal(one["out"].view(torch.int16), out_c.view(torch.int16))
     if _same_sums(wl, act_mode):
         assert torch.equal(one["y_slots"].view(torch.int16), y_ref.view(torch.int16))
         assert torch.equal(one["out"].view(torch.int16), out_ref.view(torch.int16))
@@ -227,6 +234,8 @@ def test_layer_one_call_matches_the_calls(moe, T):
     dict(T=8, H=256, E=4, K=2, I=128, has_shared=True),       # smallest H and I, few groups
     dict(T=7, H=1024, E=16, K=4, I=1024, has_shared=False),
     dict(T=3, H=512, E=16, K=4, I=256, has_shared=True),      # gate_up K split in the calls
+    dict(T=3, H=1024, E=32, K=4, I=1024, has_shared=True),    # down + combine in one launch, I = 1024
+    dict(T=8, H=512, E=16, K=4, I=256, has_shared=True),      # down + combine with 8 staged rows
     dict(T=1, H=2048, E=512, K=1, I=512, has_shared=False),   # one slot
     dict(T=7, H=4096, E=16, K=4, I=1024, has_shared=False),   # no decode kernels: the calls' path
     dict(T=40, H=512, E=16, K=4, I=256, has_shared=True),     # T > 8: the calls' path
@@ -245,6 +254,11 @@ def test_layer_one_call_arms_and_gate(moe):
         _layer_vs_calls(moe, wl, act_mode=act_mode)
     _layer_vs_calls(moe, wl, act_mode=1, gate=g)
     _layer_vs_calls(moe, wl, act_mode=0, gate=g)
+    wl2 = workload_for("decode", T=2)   # the gated combine inside the down launch
+    g2 = torch.from_numpy(np.array([-1.5, 2.0], dtype=np.float32)).cuda()
+    flush("moe_layer gated, down + combine in one launch")
+    _layer_vs_calls(moe, wl2, act_mode=0, gate=g2)
+    _layer_vs_calls(moe, wl2, act_mode=1, gate=g2)
 
 
 def test_layer_one_call_ties_and_invalid_rows(moe):
