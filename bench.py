@@ -3,9 +3,10 @@
 
 A step is one whole layer call -- router top-K, permutation, expert FFN
 (gate_up + SiLU + down, routed experts and the shared expert) and combine,
-through moe_layer (for decode batches three kernels: every block of the
-gate_up kernel routes and permutes the batch itself, then down, then the
-combine) -- over one batch of synthetic tokens already resident in HBM.  The
+through moe_layer (for decode batches two or three kernels: every block of
+the gate_up kernel routes and permutes the batch itself; then down and the
+combine, as one launch up to 48 active groups) -- over one batch of synthetic
+tokens already resident in HBM.  The
 same step through the four separate entry points is timed beside it
 (us_unfused).
 
