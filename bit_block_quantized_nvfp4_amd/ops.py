@@ -316,7 +316,7 @@ def moe_layer(W: NVFP4Weights, x: torch.Tensor, logits: torch.Tensor, K: int,
               perm=None, y_slots: Optional[torch.Tensor] = None,
               out: Optional[torch.Tensor] = None) -> dict:
     """One layer call: route -> permute -> expert FFN -> combine, all on the GPU.
-    fused=True is the C entry moe_layer (three kernels for decode batches; the
+    fused=True is the C entry moe_layer (two or three kernels for decode batches; the
     permutation's outputs in `perm` = (ids, w, counts, offsets, sorted_slot,
     slot_pos, groups) when given); fused=False runs the four separate entry
     points.  Both give the same results."""

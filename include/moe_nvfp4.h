@@ -290,11 +290,12 @@ int moe_expert_ffn_combine(const moe_nvfp4_weights* W, const uint16_t* x, int T,
  * remaining ~0.56 %": router top-k, the permutation, the routed and shared
  * experts, the combine), with the same outputs bit for bit.  For decode
  * batches (T <= 8, the bf16 or the FP8 row arm, H / 128 in {2, 4, 8, 16} and
- * I / 128 in {1, 2, 4, 8}) it runs three kernels: every block of the gate_up
- * kernel routes and permutes the batch itself in LDS, so the routing costs no
- * launch of its own (the launch structure of the decode item A2 of the page
- * "handover briefs": top-10 + shared in one launch per projection); other
- * calls run the route+permute and the FFN + combine kernels.
+ * I / 128 in {1, 2, 4, 8}) it runs two or three kernels: every block of the
+ * gate_up kernel routes and permutes the batch itself in LDS, so the routing
+ * costs no launch of its own (the launch structure of the decode item A2 of
+ * the page "handover briefs": top-10 + shared in one launch per projection);
+ * then down and the combine, in one launch while at most 48 groups are
+ * active.  Other calls run the route+permute and the FFN + combine kernels.
  *
  *   logits [T][E] float32                           (in)  router scores
  *   x, W, K, act_mode, gate                         (in)  as moe_expert_ffn_combine
