@@ -83,11 +83,15 @@ __device__ __forceinline__ void rp_route(const float* __restrict__ logits, int T
   for (int e = tid; e < G; e += NT) L.cnt[e] = (e == E) ? T : 0;
   for (int i = tid; i < kRouteFuseMaxT * kRpMapWords; i += NT) (&L.bm[0][0])[i] = 0u;
   if (wv < T) {  // uniform per wave
+    // the routing waves first on their SIMDs (the decode layer kernel's row
+    // converting waves share them): T=8 layer 42.0 -> 41.75 us, T=4 29.5 -> 29.3
+    __builtin_amdgcn_s_setprio(3);
     if (write)
       route_row_topk<MAXV>(logits + (size_t)wv * E, E, K, o.ids + (size_t)wv * K,
                            o.w + (size_t)wv * K, L.ids_l + wv * K);
     else
       route_row_topk<MAXV>(logits + (size_t)wv * E, E, K, L.ids_l + wv * K, L.w_l + wv * K);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
