@@ -1494,13 +1494,15 @@ static void launch_dec_layer_gu(int ks, const moe_nvfp4_weights& W, const float*
 // fused launch has H / 16 blocks, too few once every group is long).
 constexpr int kDcMaxGroups = 48;
 
-// Whether k_dec_down_combine takes this launch: I / 128 in {2, 4, 8}, H a
-// multiple of 16, the LDS of TR h rows per wave within the CU's.
+// Dynamic LDS of k_dec_down_combine: per wave TR h rows, 16 row factors and
+// a scale run; the y copy of the S slots' 16 columns.
 static size_t dec_down_combine_lds(int T, int K, int I, int hs) {
   const int tr = T <= 1 ? 1 : (T <= 2 ? 2 : (T <= 4 ? 4 : 8));
   const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
   return (size_t)kDcWaves * ((size_t)tr * I * 2 + 64 + (size_t)I) + S * 32;
 }
+// Whether k_dec_down_combine takes this launch: I / 128 in {2, 4, 8}, H a
+// multiple of 16, at most kDcMaxGroups groups, its LDS within the CU's.
 static bool dec_down_combine_ok(int T, int K, int H, int I, int hs, int gmax) {
   const int ncd = I / 128;
   return (ncd == 2 || ncd == 4 || ncd == 8) && H % 16 == 0 && gmax <= kDcMaxGroups &&
