@@ -49,43 +49,85 @@ size_t ffn_workspace_bytes(int T, int K, int H, int I, int has_shared, int act_m
   return b + xprep_workspace_bytes(mixed_arm(act_mode) ? 2 * T : T, H);
 }
 
+namespace {
+
+// The expert FFN's workspace: the h rows [S][I] bf16 first, then for the FP8
+// arms the e4m3 rows [T][H] and row scales [T], then for the grouped path the
+// f16 rows and their epilogue factors ([T][H] and [T], or [2T][H] and [2T]
+// for the mixed arms: rows T.. for the shared expert).
+struct FfnWs {
+  uint16_t* hbuf;
+  uint8_t* xq;
+  float* xs;
+  _Float16* xh;
+  float* rowfac;
+  size_t prep_off;  // byte offset of everything after the h rows
+};
+
+FfnWs ffn_ws(void* ws, int T, int K, int H, int I, int has_shared, int act_mode) {
+  const size_t S = (size_t)T * K + (has_shared ? (size_t)T : 0);
+  uint8_t* wp = (uint8_t*)ws;
+  FfnWs b{};
+  b.hbuf = (uint16_t*)wp;
+  b.prep_off = align256(S * I * sizeof(uint16_t));
+  wp += b.prep_off;
+  if (act_mode != MOE_ACT_BF16) {
+    b.xq = wp;
+    wp += align256((size_t)T * H);
+    b.xs = (float*)wp;
+    wp += align256((size_t)T * sizeof(float));
+  }
+  const int rows = mixed_arm(act_mode) ? 2 * T : T;
+  b.xh = (_Float16*)wp;
+  b.rowfac = (float*)(wp + align256((size_t)rows * H * sizeof(_Float16)));
+  return b;
+}
+
+// The grouped path's activation arms: one, or for the mixed arms the routed
+// experts' form (rows [0, T)) and the shared expert's (rows [T, 2T)).
+void xprep_arms(const FfnWs& b, int T, int H, int act_mode, XprepArm& a, XprepArm& a2) {
+  if (!mixed_arm(act_mode)) {
+    a = XprepArm{b.xh, b.rowfac, act_mode == MOE_ACT_FP8_ROW ? 1 : 0};
+    a2 = XprepArm{nullptr, nullptr, 0};
+  } else {
+    a = XprepArm{b.xh, b.rowfac, act_mode == MOE_ACT_FP8_ROUTED ? 1 : 0};
+    a2 = XprepArm{b.xh + (size_t)T * H, b.rowfac + T, act_mode == MOE_ACT_FP8_SHARED ? 1 : 0};
+  }
+}
+
+bool ffn_is_grouped(int T, int H, int I) { return !(T <= kDecodeMaxT && decode_supported(H, I)); }
+
+// The grouped path after its activation prep.
+hipError_t launch_grouped_ffn(const moe_nvfp4_weights& W, int T, int K, const int32_t* offsets,
+                              const int32_t* sorted_slot, int act_mode, const FfnWs& b,
+                              uint16_t* y, hipStream_t s) {
+  const int H = W.H, I = W.I;
+  const bool mixed = mixed_arm(act_mode);
+  const int shared_rows = mixed ? T : 0;
+  if (fused_supported(mixed ? 2 * T : T, H, I))
+    return launch_prefill_fused(W, T, K, offsets, sorted_slot, b.xh, b.rowfac, shared_rows,
+                                b.hbuf, y, s);
+  return launch_prefill_ffn(W, T, K, offsets, sorted_slot, b.xh, b.rowfac, shared_rows, b.hbuf,
+                            y, s);
+}
+
+}  // namespace
+
 hipError_t launch_expert_ffn(const moe_nvfp4_weights& W, const uint16_t* x, int T, int K,
                              const int32_t* offsets, const int32_t* sorted_slot,
                              const int32_t* groups, int act_mode, uint16_t* y, void* ws,
                              hipStream_t s) {
   const int H = W.H, I = W.I, hs = W.has_shared ? 1 : 0;
-  const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
-  uint8_t* wp = (uint8_t*)ws;
-  uint16_t* hbuf = (uint16_t*)wp;
-  wp += align256(S * I * sizeof(uint16_t));
-  uint8_t* xq = nullptr;
-  float* xs = nullptr;
-  if (act_mode != MOE_ACT_BF16) {
-    xq = wp;
-    wp += align256((size_t)T * H);
-    xs = (float*)wp;
-    wp += align256((size_t)T * sizeof(float));
-  }
-  if (T <= kDecodeMaxT && decode_supported(H, I))
-    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, act_mode, hbuf, xq, xs, y, s);
-  const bool mixed = mixed_arm(act_mode);
-  const int rows = mixed ? 2 * T : T;
-  _Float16* xh = (_Float16*)wp;
-  float* rowfac = (float*)(wp + align256((size_t)rows * H * sizeof(_Float16)));
-  hipError_t e;
-  if (!mixed) {
-    e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_ROW, xh, rowfac, xq, xs, s);
-  } else {  // rows [0, T): the routed experts' form; rows [T, 2T): the shared expert's
-    e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_ROUTED, xh, rowfac, xq, xs, s);
-    if (e == hipSuccess)
-      e = launch_xprep(x, T, H, act_mode == MOE_ACT_FP8_SHARED, xh + (size_t)T * H, rowfac + T,
-                       xq, xs, s);
-  }
+  const FfnWs b = ffn_ws(ws, T, K, H, I, hs, act_mode);
+  if (!ffn_is_grouped(T, H, I))
+    return launch_decode_ffn(W, x, T, K, offsets, sorted_slot, groups, act_mode, b.hbuf, b.xq,
+                             b.xs, y, s);
+  XprepArm a, a2;
+  xprep_arms(b, T, H, act_mode, a, a2);
+  hipError_t e = launch_xprep(x, T, H, a.fp8 != 0, a.xh, a.unmul, b.xq, b.xs, s);
+  if (e == hipSuccess && a2.xh) e = launch_xprep(x, T, H, a2.fp8 != 0, a2.xh, a2.unmul, b.xq, b.xs, s);
   if (e != hipSuccess) return e;
-  const int shared_rows = mixed ? T : 0;
-  if (fused_supported(rows, H, I))
-    return launch_prefill_fused(W, T, K, offsets, sorted_slot, xh, rowfac, shared_rows, hbuf, y, s);
-  return launch_prefill_ffn(W, T, K, offsets, sorted_slot, xh, rowfac, shared_rows, hbuf, y, s);
+  return launch_grouped_ffn(W, T, K, offsets, sorted_slot, act_mode, b, y, s);
 }
 
 // The expert FFN followed by the combine kernel, as one call.  (Folding the
@@ -108,9 +150,12 @@ hipError_t launch_expert_ffn_combine(const moe_nvfp4_weights& W, const uint16_t*
 }
 
 // The whole layer in one call.  Decode batches of the bf16 or FP8 row arm
-// run three kernels (routing + permutation + gate_up, down, combine); other
-// calls run route+permute, then the expert FFN and the combine.  The
-// workspace serves the permutation first and the FFN after it (stream order).
+// run three kernels (routing + permutation + gate_up, down, combine).  Larger
+// batches on the grouped path run the routing and the activation prep as one
+// launch, then the permutation, the grouped FFN and the combine.  Other calls
+// run route+permute, then the expert FFN and the combine.  The workspace
+// serves the permutation first and the FFN after it (stream order); the
+// activation prep's part of it lies after the permutation's.
 size_t layer_workspace_bytes(int T, int E, int K, int H, int I, int has_shared, int act_mode) {
   const size_t a = permute_workspace_bytes(T, E, K);
   const size_t b = ffn_combine_workspace_bytes(T, K, H, I, has_shared, act_mode);
@@ -135,6 +180,22 @@ hipError_t launch_layer(const moe_nvfp4_weights& W, const float* logits, const u
     }
     return launch_decode_layer(W, logits, x, T, K, act_mode, gate, ro, hbuf, xq, xs, y_slots, out,
                                s);
+  }
+  const FfnWs b = ffn_ws(ws, T, K, H, I, hs, act_mode);
+  if (T > kRouteFuseMaxT && ffn_is_grouped(T, H, I) && permute_workspace_bytes(T, E, K) <= b.prep_off) {
+    // the routing and the activation prep in one launch (their outputs lie
+    // after the permutation's part of the workspace), then the permutation,
+    // the grouped FFN and the combine
+    XprepArm a, a2;
+    xprep_arms(b, T, H, act_mode, a, a2);
+    hipError_t e = launch_route_xprep(logits, T, E, K, ro.ids, ro.w, x, H, a, a2, b.xq, b.xs, s);
+    if (e == hipSuccess)
+      e = launch_permute(ro.ids, T, E, K, hs, ro.counts, ro.offsets, ro.sorted_slot, ro.slot_pos,
+                         ro.groups, ws, s);
+    if (e == hipSuccess)
+      e = launch_grouped_ffn(W, T, K, ro.offsets, ro.sorted_slot, act_mode, b, y_slots, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(y_slots, ro.w, ro.slot_pos, gate, T, K, H, hs, out, s);
   }
   hipError_t e = launch_route_permute(logits, T, E, K, hs, ro.ids, ro.w, ro.counts, ro.offsets,
                                       ro.sorted_slot, ro.slot_pos, ro.groups, ws, s);

@@ -35,6 +35,18 @@ void register_ffn_kernels(std::vector<const void*>& k);
 // Launchers. Arguments are validated by the C entry points before these run.
 hipError_t launch_route_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                              hipStream_t s);
+// One activation arm of the grouped path's prep: f16 rows and epilogue
+// factors, e4m3 row quantisation when fp8 != 0.
+struct XprepArm {
+  _Float16* xh;
+  float* unmul;
+  int fp8;
+};
+// launch_route_topk and launch_xprep of one or two arms (b.xh == nullptr: one)
+// as one launch (moe_route.hip).
+hipError_t launch_route_xprep(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                              const uint16_t* x, int H, XprepArm a, XprepArm b, uint8_t* xq,
+                              float* xs, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int K);
 // Batches up to this many tokens (one per wave) are routed and permuted by
