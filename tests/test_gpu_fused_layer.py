@@ -261,6 +261,20 @@ def test_layer_one_call_arms_and_gate(moe):
     _layer_vs_calls(moe, wl2, act_mode=1, gate=g2)
 
 
+@pytest.mark.parametrize("I", [512, 256])   # the fused prefill kernel, and the two-launch one
+@pytest.mark.parametrize("act_mode", [0, 1, 2, 3])
+def test_layer_grouped_path_arms_and_gate(moe, act_mode, I):
+    """Batches above 8 tokens: the routing and the activation prep (one arm,
+    or two for the per-class arms 2 and 3) share one launch; the layer equals
+    the separate calls bit for bit, with and without the shared-expert gate."""
+    T = 72
+    wl = make_workload("lg", T=T, H=512, E=32, K=4, I=I, has_shared=True, seed=17 + act_mode)
+    flush(f"moe_layer grouped path act_mode={act_mode} I={I}")
+    _layer_vs_calls(moe, wl, act_mode=act_mode)
+    g = torch.from_numpy(np.linspace(-2.5, 2.5, T).astype(np.float32)).cuda()
+    _layer_vs_calls(moe, wl, act_mode=act_mode, gate=g)
+
+
 def test_layer_one_call_ties_and_invalid_rows(moe):
     """All-equal, NaN and -inf logit rows: the layer's routing is the router
     stage's rule in every block, and block 0 publishes it."""
