@@ -166,22 +166,10 @@ hipError_t launch_layer(const moe_nvfp4_weights& W, const float* logits, const u
                         int K, int act_mode, const float* gate, const RpOut& ro,
                         uint16_t* y_slots, uint16_t* out, void* ws, hipStream_t s) {
   const int H = W.H, I = W.I, E = W.E, hs = W.has_shared ? 1 : 0;
-  if (decode_layer_supported(T, E, K, H, I, act_mode)) {
-    const size_t S = (size_t)T * K + (hs ? (size_t)T : 0);
-    uint8_t* wp = (uint8_t*)ws;
-    uint16_t* hbuf = (uint16_t*)wp;
-    wp += align256(S * I * sizeof(uint16_t));
-    uint8_t* xq = nullptr;
-    float* xs = nullptr;
-    if (act_mode != MOE_ACT_BF16) {
-      xq = wp;
-      wp += align256((size_t)T * H);
-      xs = (float*)wp;
-    }
-    return launch_decode_layer(W, logits, x, T, K, act_mode, gate, ro, hbuf, xq, xs, y_slots, out,
-                               s);
-  }
   const FfnWs b = ffn_ws(ws, T, K, H, I, hs, act_mode);
+  if (decode_layer_supported(T, E, K, H, I, act_mode))
+    return launch_decode_layer(W, logits, x, T, K, act_mode, gate, ro, b.hbuf, b.xq, b.xs, y_slots,
+                               out, s);
   if (T > kRouteFuseMaxT && ffn_is_grouped(T, H, I) && permute_workspace_bytes(T, E, K) <= b.prep_off) {
     // the routing and the activation prep in one launch (their outputs lie
     // after the permutation's part of the workspace), then the permutation,
